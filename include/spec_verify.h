@@ -1,0 +1,224 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) batched lossless token
+ * verification library (libspecverify.so).
+ *
+ * What it computes
+ * ----------------
+ * Speculative decoding lets a cheap draft propose tokens that the expensive
+ * target verifies in parallel ("Technische Zusammenfassung: HiSpec:
+ * Hierarchische spekulatives Decodieren fuer LLMs", gist.science 2510.01336,
+ * section 1 "Problemstellung"; "Speculative Speculative Decoding",
+ * gist.science 2603.03251, Technische Zusammenfassung section 1).  Verification
+ * is lossless when it applies the standard speculative-sampling rule, whose
+ * proof the HiSpec summary invokes for each of its stages (section 2, bullet
+ * "Verlustfreie Garantie"):
+ *
+ *   - drafted token x at position j is accepted with probability
+ *     min(1, p_j(x) / q_j(x)), p = target distribution, q = draft distribution;
+ *   - at the first rejection a token is resampled from norm(max(0, p_j - q_j)),
+ *     the residual proportional to target minus draft (SSD summary section 3.B);
+ *   - when every draft is accepted a bonus token is drawn from the next target
+ *     row (SSD summary section 2, item 1).
+ *
+ * spec_verify_hier adds HiSpec's two-stage verification L_d -> L_i -> L_f
+ * (HiSpec summary section 2 "Kernmechanismus", bullets "Verlustfreie Garantie"
+ * and "Dynamische Verifizierungsrichtlinie"): the intermediate exit L_i
+ * verifies the drafts of the shallow exit L_d and tentatively accepts them, the
+ * final exit L_f then verifies the tentative tokens in windows of N_i
+ * positions.  kv_blocktable_truncate drops the KV slots of rejected tokens from
+ * a paged block table without recomputation or padding (HiSpec summary
+ * section 2, bullets "Wiederverwendung von KV-Cache ..." and "Unterstuetzung
+ * fuer Batch-Inferenz").
+ *
+ * Distributions are softmax(logits / temperature) per row, computed from the
+ * logits inside the library; temperature 0 means greedy (one-hot at the
+ * lowest-index maximum), which reduces the rule to an argmax prefix match.
+ *
+ * Uniforms come from Philox4x32-10 (Salmon et al., SC'11): one block per
+ * (position j, sequence b, stage s, call offset) with counter
+ * (j, b, s, offset) and key (seed low 32 bits, seed high 32 bits).  Word 0
+ * gives the accept uniform u = (w0 >> 8) * 2^-24, word 1 the draw uniform
+ * v = (w1 >> 8) * 2^-24.  Stage 0 is the single stage and stage 1 of the
+ * hierarchy, stage 1 is its second stage.  Same inputs, seed and offset give
+ * bit-identical outputs.
+ *
+ * Conventions
+ * -----------
+ * Ownership: every data pointer is caller-owned device memory (or host memory
+ * where stated).  The library never allocates, frees or keeps device memory;
+ * scratch comes from the caller's workspace, sized by
+ * spec_verify_workspace_bytes.  Inputs are read-only; outputs are written.
+ *
+ * Layout: logits are row-major [B, P, V] (P = k for the draft exit, k + 1 for
+ * the others), element type float32 or bfloat16, consecutive (b, j) rows
+ * row_stride elements apart (row_stride >= V; 0 means V).  Rows that start on
+ * a 16-byte boundary are streamed with 128-bit loads, other rows with scalar
+ * loads (correct, slower).  Tokens and counts are int32.
+ *
+ * Asynchrony: calls enqueue work on hip_stream (a hipStream_t; NULL = the null
+ * stream) and return without synchronising; outputs are valid once the stream
+ * has reached that point.  spec_verify_device_status synchronises.
+ *
+ * Errors: every call returns an SV_* status.  Arguments are validated on the
+ * host before any launch; a failing call launches nothing and writes nothing,
+ * and spec_verify_last_error() (thread-local) describes the failure.  No C++
+ * exception crosses this interface.  Data problems only visible on the device
+ * (a token outside [0, V), a negative or NaN temperature) do not fail the call:
+ * the token is rejected (it has probability 0), the sequence is treated as
+ * greedy, and a bit is set in the workspace flags (spec_verify_device_status).
+ *
+ * Thread safety: calls are reentrant; concurrent calls must use distinct
+ * workspaces and outputs.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_VERIFY_ABI_VERSION 1
+
+/* Status codes. */
+#define SV_OK 0
+#define SV_ERR_INVALID_ARG 1 /* NULL pointer, negative size, row_stride < V, window < 1 ... */
+#define SV_ERR_UNSUPPORTED 2 /* dtype, k > SV_MAX_DRAFT, V > SV_MAX_VOCAB            */
+#define SV_ERR_MISALIGNED 3  /* pointer not aligned to its element size               */
+#define SV_ERR_WORKSPACE 4   /* workspace NULL, too small, or not 256-byte aligned     */
+#define SV_ERR_DEVICE 5      /* a HIP call failed; its text is in spec_verify_last_error */
+
+/* Element types of logits. */
+#define SV_DTYPE_F32 0
+#define SV_DTYPE_BF16 1
+
+/* Limits. */
+#define SV_MAX_DRAFT 63        /* k + 1 positions fit one 64-lane wavefront */
+#define SV_MAX_VOCAB (1 << 20) /* inverse-CDF tile sums stay in LDS          */
+
+/* Device flags (spec_verify_device_status). */
+#define SV_FLAG_TOKEN_RANGE 1u /* a drafted token outside [0, V) was rejected        */
+#define SV_FLAG_TEMPERATURE 2u /* a negative or NaN temperature was treated as 0    */
+
+typedef struct {
+  int32_t batch;      /* B >= 0 sequences (0: nothing to do)                  */
+  int32_t num_draft;  /* k in [0, SV_MAX_DRAFT] drafted tokens per sequence    */
+  int32_t vocab;      /* V in [1, SV_MAX_VOCAB]                                 */
+  int32_t dtype;      /* SV_DTYPE_F32 or SV_DTYPE_BF16 (all exits alike)       */
+  int64_t row_stride; /* elements between consecutive rows; 0 => V             */
+  uint64_t seed;      /* Philox key: low 32 bits = k0, high 32 bits = k1       */
+  uint32_t offset;    /* Philox counter word 3: a call / step index            */
+  uint32_t reserved;  /* must be 0                                             */
+} spec_verify_desc;
+
+/* Optional per-call diagnostics, for parity checks.  Every field is a device
+ * pointer (or, for the events, a hipEvent_t handle) or NULL.  Entries that do
+ * not apply (untested positions, stages without a draw) are NaN.  Stage index 0 = single stage / hierarchy stage 1,
+ * 1 = hierarchy stage 2. */
+typedef struct {
+  float* uniforms;   /* [B, 2, k+1, 2]: (u, v) of each position                   */
+  double* probs;     /* [B, 2, k+1, 2]: (p(t_j), q(t_j)) of each tested position    */
+  double* draws;     /* [B, 2, 4]: (R, v*R, C(y-1), C(y)) of each stage's draw      */
+  void* stats_begin; /* hipEvent_t recorded on hip_stream right before the
+                        row-statistics kernel (the HBM stream), or NULL          */
+  void* stats_end;   /* hipEvent_t recorded right after it, or NULL               */
+} spec_verify_diag;
+
+/* Version of this header's ABI (SPEC_VERIFY_ABI_VERSION). */
+int32_t spec_verify_abi_version(void);
+
+/* Static text for a status code. */
+const char* spec_verify_status_string(int32_t status);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* spec_verify_last_error(void);
+
+/* Workspace bytes a call needs: num_exits = 2 (spec_verify_single) or 3
+ * (spec_verify_hier).  0 if the descriptor is invalid.  Pure host code. */
+size_t spec_verify_workspace_bytes(const spec_verify_desc* desc, int32_t num_exits);
+
+/* Host-side validation of a descriptor, window and workspace size, exactly as
+ * the verify calls perform it (no pointers checked).  Pure host code: callable
+ * without a GPU.  window is ignored for num_exits = 2. */
+int32_t spec_verify_validate(const spec_verify_desc* desc, int32_t num_exits, int32_t window,
+                             size_t workspace_bytes);
+
+/* Single-stage verify: draft q vs target p (standard rule, bonus from p_k).
+ *   draft_logits   [B, k, V]   device, read-only
+ *   target_logits  [B, k+1, V] device, read-only
+ *   draft_tokens   [B, k]      device int32
+ *   temperature    [B]         device float32, NULL => all 1.0; 0 => greedy
+ *   accept_len     [B]         out: accepted drafts a in [0, k]
+ *   out_tokens     [B, k+1]    out: the a accepted drafts then the correction
+ *                              or bonus token; -1 after the a+1 emitted tokens
+ *   num_emitted    [B]         out: a + 1
+ *   num_drop       [B]         out or NULL: k - a drafted KV slots to roll back
+ *   packed_tokens  [B*(k+1)]   out or NULL: emitted tokens of all sequences
+ *                              back to back (no padding)
+ *   cu_offsets     [B+1]       out or NULL (required with packed_tokens):
+ *                              sequence b's tokens are packed[cu[b] .. cu[b+1])
+ *   workspace      device scratch, 256-byte aligned, >= spec_verify_workspace_bytes(desc, 2)
+ *   diag           host pointer to a spec_verify_diag, or NULL
+ */
+int32_t spec_verify_single(const spec_verify_desc* desc, const void* draft_logits,
+                           const void* target_logits, const int32_t* draft_tokens,
+                           const float* temperature, int32_t* accept_len, int32_t* out_tokens,
+                           int32_t* num_emitted, int32_t* num_drop, int32_t* packed_tokens,
+                           int32_t* cu_offsets, void* workspace, size_t workspace_bytes,
+                           const spec_verify_diag* diag, void* hip_stream);
+
+/* Hierarchical verify L_d -> L_i -> L_f.
+ * Stage 1: the standard rule with q = L_d rows 0..k-1, p = L_i rows 0..k; it
+ *   yields a1 accepted drafts and one L_i token (correction, or the bonus from
+ *   L_i row k), the tentative sequence t of length a1 + 1.
+ * Stage 2: the standard rule with t as the draft, q = L_i and p = L_f rows
+ *   0..a1, visited in windows of `window` positions; a2 = first rejection
+ *   (else a1 + 1).  On a rejection the L_f correction is drawn from
+ *   max(0, L_f - L_i) at a2; no L_f bonus is drawn (L_f's distribution after
+ *   t is not an input).
+ * Emitted: n = min(a1, a2) + 1 tokens; num_drop = k - (n - 1).
+ *   ld_logits [B, k, V], li_logits and lf_logits [B, k+1, V]: device, read-only
+ *   accept_len_inter [B] out: a1;  accept_len_final [B] out: a2
+ *   other arguments as for spec_verify_single; workspace sized with num_exits = 3
+ */
+int32_t spec_verify_hier(const spec_verify_desc* desc, int32_t window, const void* ld_logits,
+                         const void* li_logits, const void* lf_logits,
+                         const int32_t* draft_tokens, const float* temperature,
+                         int32_t* accept_len_inter, int32_t* accept_len_final,
+                         int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                         int32_t* packed_tokens, int32_t* cu_offsets, void* workspace,
+                         size_t workspace_bytes, const spec_verify_diag* diag,
+                         void* hip_stream);
+
+/* Paged-KV rollback after verification.  Sequence b holds seq_lens[b] KV slots
+ * in blocks of block_size slots listed by block_table[b, 0..max_blocks) (-1 =
+ * empty).  Its last num_drop[b] slots are dropped: the new length is
+ * L' = L - num_drop; logical blocks ceil(L'/bs) .. ceil(L/bs)-1 no longer hold
+ * a slot, so their ids are written to freed_blocks[b, ...] in ascending
+ * logical order (-1 padded to max_freed), num_freed[b] is their count, and
+ * their table entries become -1.  Partly used blocks are kept.
+ *   block_table  [B, max_blocks] device int32, in/out
+ *   seq_lens     [B]             device int32, in/out
+ *   num_drop     [B]             device int32 (e.g. the verify call's num_drop)
+ *   freed_blocks [B, max_freed]  device int32, out (may be NULL if max_freed == 0)
+ *   num_freed    [B]             device int32, out
+ * A sequence whose num_drop lies outside [0, L], whose L exceeds
+ * max_blocks * block_size, or that would free more than max_freed blocks is
+ * left unchanged and gets num_freed[b] = -1.
+ */
+int32_t kv_blocktable_truncate(int32_t batch, int32_t max_blocks, int32_t block_size,
+                               int32_t* block_table, int32_t* seq_lens,
+                               const int32_t* num_drop, int32_t* freed_blocks,
+                               int32_t max_freed, int32_t* num_freed, void* hip_stream);
+
+/* Synchronises hip_stream, then copies the device flags (SV_FLAG_*) of the
+ * last verify call that used `workspace` into *flags_out (host). */
+int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,311 @@
+// C ABI of libspecverify.so: host-side validation, workspace layout and the
+// launch sequence of each call.  See include/spec_verify.h for the contract.
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "spec_verify.h"
+#include "sv_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Plan {
+  int num_exits = 0;
+  int64_t rows_total = 0;
+  int nc = 0;
+  int64_t ld = 0;
+  size_t ws_bytes = 0;
+  int32_t exit_pos[3] = {0, 0, 0};
+  int32_t exit_row0[3] = {0, 0, 0};
+};
+
+// Validates the descriptor and derives the launch plan.  Pure host code.
+int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
+  if (!d) return fail(SV_ERR_INVALID_ARG, "desc is NULL");
+  if (num_exits != 2 && num_exits != 3) return fail(SV_ERR_INVALID_ARG, "num_exits must be 2 or 3");
+  if (d->reserved != 0) return fail(SV_ERR_INVALID_ARG, "desc.reserved must be 0");
+  if (d->batch < 0) return fail(SV_ERR_INVALID_ARG, "batch < 0");
+  if (d->num_draft < 0) return fail(SV_ERR_INVALID_ARG, "num_draft < 0");
+  if (d->num_draft > SV_MAX_DRAFT)
+    return fail(SV_ERR_UNSUPPORTED, "num_draft > " + std::to_string(SV_MAX_DRAFT));
+  if (d->vocab < 1) return fail(SV_ERR_INVALID_ARG, "vocab < 1");
+  if (d->vocab > SV_MAX_VOCAB)
+    return fail(SV_ERR_UNSUPPORTED, "vocab > " + std::to_string(SV_MAX_VOCAB));
+  if (d->dtype != SV_DTYPE_F32 && d->dtype != SV_DTYPE_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "dtype must be SV_DTYPE_F32 or SV_DTYPE_BF16");
+  const int64_t ld = d->row_stride == 0 ? d->vocab : d->row_stride;
+  if (ld < d->vocab) return fail(SV_ERR_INVALID_ARG, "row_stride < vocab");
+  if (ld > (int64_t(1) << 40)) return fail(SV_ERR_INVALID_ARG, "row_stride too large");
+  const int k = d->num_draft;
+  p->num_exits = num_exits;
+  p->exit_pos[0] = k;
+  p->exit_pos[1] = k + 1;
+  p->exit_pos[2] = num_exits == 3 ? k + 1 : 0;
+  const int64_t B = d->batch;
+  p->exit_row0[0] = 0;
+  p->rows_total = B * k;
+  for (int e = 1; e < num_exits; ++e) {
+    if (p->rows_total > INT32_MAX) break;
+    p->exit_row0[e] = static_cast<int32_t>(p->rows_total);
+    p->rows_total += B * (k + 1);
+  }
+  const int ce = sv::chunk_elems(d->dtype);
+  p->nc = (d->vocab + ce - 1) / ce;
+  if (p->rows_total > INT32_MAX || p->rows_total * p->nc > INT32_MAX)
+    return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
+  p->ld = ld;
+  p->ws_bytes = sv::kFlagsBytes + static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
+  return SV_OK;
+}
+
+int32_t check_workspace(const Plan& p, const void* ws, size_t bytes) {
+  if (!ws) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned_to(ws, 256)) return fail(SV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (bytes < p.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "workspace has " + std::to_string(bytes) + " bytes, needs " +
+                                      std::to_string(p.ws_bytes));
+  return SV_OK;
+}
+
+int32_t check_logits(const void* ptr, int rows, int dtype, const char* name) {
+  if (rows == 0) return SV_OK;
+  if (!ptr) return fail(SV_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned_to(ptr, sv::elem_bytes(dtype)))
+    return fail(SV_ERR_MISALIGNED, std::string(name) + " not aligned to its element size");
+  return SV_OK;
+}
+
+int32_t check_i32(const void* ptr, bool required, const char* name) {
+  if (!ptr) return required ? fail(SV_ERR_INVALID_ARG, std::string(name) + " is NULL") : SV_OK;
+  if (!aligned_to(ptr, 4)) return fail(SV_ERR_MISALIGNED, std::string(name) + " not 4-byte aligned");
+  return SV_OK;
+}
+
+int32_t check_diag(const spec_verify_diag* diag) {
+  if (!diag) return SV_OK;
+  if (diag->uniforms && !aligned_to(diag->uniforms, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.uniforms not 4-byte aligned");
+  if (diag->probs && !aligned_to(diag->probs, 8))
+    return fail(SV_ERR_MISALIGNED, "diag.probs not 8-byte aligned");
+  if (diag->draws && !aligned_to(diag->draws, 8))
+    return fail(SV_ERR_MISALIGNED, "diag.draws not 8-byte aligned");
+  return SV_OK;
+}
+
+int32_t device_error(hipError_t e, const char* what) {
+  return fail(SV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define SV_TRY(expr)              \
+  do {                            \
+    const int32_t _s = (expr);    \
+    if (_s != SV_OK) return _s;   \
+  } while (0)
+
+int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t window,
+                   const void* const* logits, const int32_t* tokens, const float* temperature,
+                   int32_t* accept_len, int32_t* accept_len_final, int32_t* out_tokens,
+                   int32_t* num_emitted, int32_t* num_drop, int32_t* packed, int32_t* cu_offsets,
+                   void* workspace, size_t workspace_bytes, const spec_verify_diag* diag,
+                   void* hip_stream) {
+  Plan p;
+  SV_TRY(make_plan(desc, num_exits, &p));
+  if (num_exits == 3 && window < 1) return fail(SV_ERR_INVALID_ARG, "window < 1");
+  static const char* names[3] = {"draft/L_d logits", "target/L_i logits", "L_f logits"};
+  for (int e = 0; e < num_exits; ++e)
+    SV_TRY(check_logits(logits[e], desc->batch * p.exit_pos[e], desc->dtype, names[e]));
+  const bool any = desc->batch > 0;
+  SV_TRY(check_i32(tokens, any && desc->num_draft > 0, "draft_tokens"));
+  if (temperature && !aligned_to(temperature, 4))
+    return fail(SV_ERR_MISALIGNED, "temperature not 4-byte aligned");
+  SV_TRY(check_i32(accept_len, any, "accept_len"));
+  if (num_exits == 3) SV_TRY(check_i32(accept_len_final, any, "accept_len_final"));
+  SV_TRY(check_i32(out_tokens, any, "out_tokens"));
+  SV_TRY(check_i32(num_emitted, any, "num_emitted"));
+  SV_TRY(check_i32(num_drop, false, "num_drop"));
+  SV_TRY(check_i32(packed, false, "packed_tokens"));
+  SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
+  if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
+  SV_TRY(check_diag(diag));
+  SV_TRY(check_workspace(p, workspace, workspace_bytes));
+  if (!any) return SV_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  uint32_t* flags = static_cast<uint32_t*>(workspace);
+  sv::Partial* partials =
+      reinterpret_cast<sv::Partial*>(static_cast<char*>(workspace) + sv::kFlagsBytes);
+
+  sv::RowStatsArgs ra{};
+  for (int e = 0; e < 3; ++e) {
+    ra.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+    ra.exit_pos[e] = p.exit_pos[e];
+    ra.exit_row0[e] = e < num_exits ? p.exit_row0[e] : INT32_MAX;
+  }
+  ra.num_exits = num_exits;
+  ra.V = desc->vocab;
+  ra.ld = p.ld;
+  ra.nc = p.nc;
+  ra.dtype = desc->dtype;
+  ra.temperature = temperature;
+  ra.partials = partials;
+  ra.flags = flags;
+  hipError_t err;
+  if (diag && diag->stats_begin) {
+    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
+    if (err != hipSuccess) return device_error(err, "event record");
+  }
+  err = sv::launch_rowstats(ra, static_cast<int>(p.rows_total), st);
+  if (err != hipSuccess) return device_error(err, "row statistics launch");
+  if (diag && diag->stats_end) {
+    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
+    if (err != hipSuccess) return device_error(err, "event record");
+  }
+
+  sv::VerifyArgs va{};
+  va.hier = num_exits == 3;
+  va.B = desc->batch;
+  va.k = desc->num_draft;
+  va.V = desc->vocab;
+  va.dtype = desc->dtype;
+  va.nc = p.nc;
+  va.window = num_exits == 3 ? window : 1;
+  va.ld = p.ld;
+  for (int e = 0; e < 3; ++e) {
+    va.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+    va.exit_row0[e] = e < num_exits ? p.exit_row0[e] : 0;
+  }
+  va.partials = partials;
+  va.tokens = tokens;
+  va.temperature = temperature;
+  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  va.offset = desc->offset;
+  va.accept_len = accept_len;
+  va.accept_len_final = num_exits == 3 ? accept_len_final : nullptr;
+  va.out_tokens = out_tokens;
+  va.num_emitted = num_emitted;
+  va.num_drop = num_drop;
+  va.diag_uniforms = diag ? diag->uniforms : nullptr;
+  va.diag_probs = diag ? diag->probs : nullptr;
+  va.diag_draws = diag ? diag->draws : nullptr;
+  va.flags = flags;
+  err = sv::launch_verify(va, st);
+  if (err != hipSuccess) return device_error(err, "verify launch");
+
+  if (packed) {
+    sv::PackArgs pa{desc->batch, desc->num_draft, out_tokens, num_emitted, packed, cu_offsets};
+    err = sv::launch_pack(pa, st);
+    if (err != hipSuccess) return device_error(err, "pack launch");
+  }
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t spec_verify_abi_version(void) { return SPEC_VERIFY_ABI_VERSION; }
+
+const char* spec_verify_status_string(int32_t status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID_ARG: return "SV_ERR_INVALID_ARG";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    case SV_ERR_MISALIGNED: return "SV_ERR_MISALIGNED";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE";
+    case SV_ERR_DEVICE: return "SV_ERR_DEVICE";
+    default: return "SV_ERR_UNKNOWN";
+  }
+}
+
+const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
+
+size_t spec_verify_workspace_bytes(const spec_verify_desc* desc, int32_t num_exits) {
+  Plan p;
+  const std::string keep = g_last_error;
+  const int32_t s = make_plan(desc, num_exits, &p);
+  g_last_error = keep;
+  return s == SV_OK ? p.ws_bytes : 0;
+}
+
+int32_t spec_verify_validate(const spec_verify_desc* desc, int32_t num_exits, int32_t window,
+                             size_t workspace_bytes) {
+  Plan p;
+  SV_TRY(make_plan(desc, num_exits, &p));
+  if (num_exits == 3 && window < 1) return fail(SV_ERR_INVALID_ARG, "window < 1");
+  if (workspace_bytes < p.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, needs " + std::to_string(p.ws_bytes));
+  return SV_OK;
+}
+
+int32_t spec_verify_single(const spec_verify_desc* desc, const void* draft_logits,
+                           const void* target_logits, const int32_t* draft_tokens,
+                           const float* temperature, int32_t* accept_len, int32_t* out_tokens,
+                           int32_t* num_emitted, int32_t* num_drop, int32_t* packed_tokens,
+                           int32_t* cu_offsets, void* workspace, size_t workspace_bytes,
+                           const spec_verify_diag* diag, void* hip_stream) {
+  const void* logits[3] = {draft_logits, target_logits, nullptr};
+  return run_verify(desc, 2, 1, logits, draft_tokens, temperature, accept_len, nullptr, out_tokens,
+                    num_emitted, num_drop, packed_tokens, cu_offsets, workspace, workspace_bytes,
+                    diag, hip_stream);
+}
+
+int32_t spec_verify_hier(const spec_verify_desc* desc, int32_t window, const void* ld_logits,
+                         const void* li_logits, const void* lf_logits,
+                         const int32_t* draft_tokens, const float* temperature,
+                         int32_t* accept_len_inter, int32_t* accept_len_final,
+                         int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                         int32_t* packed_tokens, int32_t* cu_offsets, void* workspace,
+                         size_t workspace_bytes, const spec_verify_diag* diag,
+                         void* hip_stream) {
+  const void* logits[3] = {ld_logits, li_logits, lf_logits};
+  return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
+                    accept_len_final, out_tokens, num_emitted, num_drop, packed_tokens,
+                    cu_offsets, workspace, workspace_bytes, diag, hip_stream);
+}
+
+int32_t kv_blocktable_truncate(int32_t batch, int32_t max_blocks, int32_t block_size,
+                               int32_t* block_table, int32_t* seq_lens,
+                               const int32_t* num_drop, int32_t* freed_blocks,
+                               int32_t max_freed, int32_t* num_freed, void* hip_stream) {
+  if (batch < 0) return fail(SV_ERR_INVALID_ARG, "batch < 0");
+  if (max_blocks < 0) return fail(SV_ERR_INVALID_ARG, "max_blocks < 0");
+  if (block_size < 1) return fail(SV_ERR_INVALID_ARG, "block_size < 1");
+  if (max_freed < 0) return fail(SV_ERR_INVALID_ARG, "max_freed < 0");
+  const bool any = batch > 0;
+  SV_TRY(check_i32(block_table, any && max_blocks > 0, "block_table"));
+  SV_TRY(check_i32(seq_lens, any, "seq_lens"));
+  SV_TRY(check_i32(num_drop, any, "num_drop"));
+  SV_TRY(check_i32(freed_blocks, any && max_freed > 0, "freed_blocks"));
+  SV_TRY(check_i32(num_freed, any, "num_freed"));
+  if (!any) return SV_OK;
+  sv::KvArgs a{batch, max_blocks, block_size, max_freed, block_table, seq_lens,
+               num_drop, freed_blocks, num_freed};
+  const hipError_t err = sv::launch_kv_truncate(a, static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return device_error(err, "kv truncate launch");
+  return SV_OK;
+}
+
+int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream) {
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (!flags_out) return fail(SV_ERR_INVALID_ARG, "flags_out is NULL");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t err = hipStreamSynchronize(st);
+  if (err != hipSuccess) return device_error(err, "stream synchronize");
+  err = hipMemcpy(flags_out, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return device_error(err, "flags copy");
+  return SV_OK;
+}
+
+}  // extern "C"

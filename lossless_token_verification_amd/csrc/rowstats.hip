@@ -1,0 +1,229 @@
+// Row statistics: the HBM stream of the verification path.
+//
+// Every logit row of every exit (draft / target, or L_d / L_i / L_f) is read
+// once.  One workgroup handles one 64 KiB chunk of one row: each thread issues
+// its 16 nontemporal 128-bit loads up front, keeps the chunk in registers, and
+// reduces it to partial softmax statistics:
+//   temperature > 0: c = round(max * s) and S = sum 2^(l * s - c), with
+//                    s = log2(e) / temperature (fp32 exponent, fp64 sum);
+//   temperature = 0: the maximum and its lowest index (greedy decoding).
+// The verify kernel merges the chunks of the rows it needs.  Softmax of a row
+// is the per-exit token distribution the rule compares ("Kernmechanismus" of
+// the HiSpec summary: the exits L_d, L_i, L_f each yield a token distribution).
+#include "sv_common.h"
+
+namespace sv {
+
+namespace {
+
+struct Red {
+  float key;
+  int idx;
+  double S;
+};
+
+// Workgroup reduction of greedy (max, lowest index) pairs.
+__device__ void block_argmax(float& m, int& idx, Red* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave);
+    const int oi = __shfl_xor(idx, o, kWave);
+    if (om > m || (om == m && oi < idx)) {
+      m = om;
+      idx = oi;
+    }
+  }
+  if (lane == 0) {
+    lds[wave].key = m;
+    lds[wave].idx = idx;
+  }
+  __syncthreads();
+  m = lds[0].key;
+  idx = lds[0].idx;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    if (lds[w].key > m || (lds[w].key == m && lds[w].idx < idx)) {
+      m = lds[w].key;
+      idx = lds[w].idx;
+    }
+  }
+}
+
+// Workgroup reduction of (c, S) partial sums: common reference max(c), then
+// each S rescaled by 2^(c_t - c) in double and summed.
+__device__ void block_logsum(float& c, double& S, Red* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  float cm = wave_max(c);
+  if (lane == 0) lds[wave].key = cm;
+  __syncthreads();
+  cm = lds[0].key;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) cm = fmaxf(cm, lds[w].key);
+  double Sr = 0.0;
+  if (S > 0.0) Sr = S * exp2(static_cast<double>(c) - static_cast<double>(cm));
+  Sr = wave_sum(Sr);
+  __syncthreads();
+  if (lane == 0) lds[wave].S = Sr;
+  __syncthreads();
+  S = lds[0].S;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) S += lds[w].S;
+  c = cm;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 4]) {
+  if constexpr (DT == 1) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  } else {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
+  constexpr int VPE = DT == 1 ? 8 : 4;
+  constexpr int ES = DT == 1 ? 2 : 4;
+  constexpr int CE = kChunkBytes / ES;
+  __shared__ Red lds[kWaves];
+
+  const int row = blockIdx.x / a.nc;
+  const int chunk = blockIdx.x - row * a.nc;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) a.flags[0] = 0u;  // flags of this call start clear
+
+  int e = 0;
+  if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
+  if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
+  const int local = row - a.exit_row0[e];
+  const int b = local / a.exit_pos[e];
+  const float tau = a.temperature ? a.temperature[b] : 1.0f;
+  const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
+  const float s = greedy ? 0.0f : kLog2e / tau;
+  const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
+  const int e0 = chunk * CE;
+  const int e1 = min(a.V, e0 + CE);
+
+  float m = -INFINITY;
+  int idx = 0x7fffffff;
+  double S = 0.0;
+  float c = -INFINITY;
+
+  if ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0) {
+    // 16-byte aligned row: vectors [e0/VPE, e0/VPE + nfull) then < VPE scalars.
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp) + e0 / VPE;
+    const int nfull = (e1 - e0) / VPE;
+    const uint32_t pad = DT == 1 ? 0xff80ff80u : 0xff800000u;  // -inf
+    u32x4 buf[kVecPerThread];
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int vi = i * kThreads + tid;
+      buf[i] = vi < nfull ? __builtin_nontemporal_load(vp + vi) : u32x4{pad, pad, pad, pad};
+    }
+    const int tail0 = e0 + nfull * VPE;
+    const bool has_tail = tid < e1 - tail0;
+    const float xt = has_tail ? load_elem(rowp, tail0 + tid, DT) : -INFINITY;
+
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      float x[VPE];
+      unpack<DT>(buf[i], x);
+#pragma unroll
+      for (int q = 0; q < VPE; q += 2) {
+        m0 = fmaxf(m0, x[q]);
+        m1 = fmaxf(m1, x[q + 1]);
+      }
+    }
+    m = fmaxf(fmaxf(m0, m1), xt);
+    const bool empty = !(m > -INFINITY);   // no finite element in this thread's share
+
+    if (greedy) {
+      // lowest index attaining the thread's maximum
+#pragma unroll
+      for (int i = kVecPerThread - 1; i >= 0; --i) {
+        float x[VPE];
+        unpack<DT>(buf[i], x);
+#pragma unroll
+        for (int q = VPE - 1; q >= 0; --q)
+          if (x[q] == m) idx = e0 + (i * kThreads + tid) * VPE + q;
+      }
+      if (idx == 0x7fffffff && has_tail && xt == m) idx = tail0 + tid;
+      if (empty) idx = 0x7fffffff;
+    } else if (!empty) {
+      c = m * s;
+      const float nc_ = -c;
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+        float x[VPE];
+        unpack<DT>(buf[i], x);
+        float t[VPE];
+#pragma unroll
+        for (int q = 0; q < VPE; ++q) t[q] = __builtin_amdgcn_exp2f(fmaf(x[q], s, nc_));
+        // pairwise within the vector, fp64 across vectors
+#pragma unroll
+        for (int w = VPE / 2; w > 0; w >>= 1)
+#pragma unroll
+          for (int q = 0; q < w; ++q) t[q] += t[q + w];
+        S += static_cast<double>(t[0]);
+      }
+      if (has_tail) S += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xt, s, nc_)));
+    }
+  } else {
+    // Misaligned row: scalar loads, two passes over the chunk.
+    for (int i = e0 + tid; i < e1; i += kThreads) {
+      const float x = load_elem(rowp, i, DT);
+      if (x > m) {
+        m = x;
+        idx = i;
+      }
+    }
+    if (!greedy && m > -INFINITY) {
+      c = m * s;
+      float acc = 0.0f;
+      int n = 0;
+      for (int i = e0 + tid; i < e1; i += kThreads) {
+        acc += __builtin_amdgcn_exp2f(fmaf(load_elem(rowp, i, DT), s, -c));
+        if (++n == 8) {
+          S += static_cast<double>(acc);
+          acc = 0.0f;
+          n = 0;
+        }
+      }
+      S += static_cast<double>(acc);
+    }
+  }
+
+  Partial out;
+  if (greedy) {
+    block_argmax(m, idx, lds);
+    out.key = m;
+    out.amax = idx;
+    out.S = 0.0;
+  } else {
+    if (!(S > 0.0)) c = -INFINITY;   // thread saw no element
+    block_logsum(c, S, lds);
+    out.key = c;
+    out.amax = -1;
+    out.S = S;
+  }
+  if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = out;
+}
+
+}  // namespace
+
+hipError_t launch_rowstats(const RowStatsArgs& a, int rows_total, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(rows_total) * static_cast<unsigned>(a.nc));
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(rowstats_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(rowstats_kernel<0>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,117 @@
+"""The C ABI on the CPU: the library loads (no GPU needed), exports every
+function include/spec_verify.h declares, and its host-side validation returns
+the documented status codes.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import lossless_token_verification_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libspecverify.so is not built (run __graft_entry__.build())")
+    m.library()
+    return m
+
+
+def test_every_declared_symbol_is_exported(sv):
+    names = declared_functions()
+    assert len(names) == 9, names
+    assert set(names) == set(sv.EXPORTED)
+    lib = ctypes.CDLL(sv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(sv):
+    lib = sv.library()
+    assert sv.abi_version() == 1
+    for code, name in ((0, b"SV_OK"), (1, b"SV_ERR_INVALID_ARG"), (2, b"SV_ERR_UNSUPPORTED"),
+                       (3, b"SV_ERR_MISALIGNED"), (4, b"SV_ERR_WORKSPACE"), (5, b"SV_ERR_DEVICE"),
+                       (99, b"SV_ERR_UNKNOWN")):
+        assert lib.spec_verify_status_string(code) == name
+
+
+def test_workspace_size_formula(sv):
+    # 256 B of flags + one 16-byte partial per (row, 64 KiB chunk)
+    assert sv.workspace_bytes(256, 8, 128256, 1, 3) == 256 + 256 * 26 * 4 * 16
+    assert sv.workspace_bytes(64, 4, 32000, 1, 2) == 256 + 64 * 9 * 1 * 16
+    assert sv.workspace_bytes(32, 5, 151936, 0, 2) == 256 + 32 * 11 * 10 * 16
+    assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
+    assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
+
+
+def _status(sv, **kw):
+    base = dict(batch=4, num_draft=3, vocab=100, dtype_code=0, row_stride=0)
+    base.update({k: v for k, v in kw.items() if k in base})
+    d = sv.make_desc(**base)
+    if "reserved" in kw:
+        d.reserved = kw["reserved"]
+    return sv.validate(d, kw.get("exits", 2), kw.get("window", 4), kw.get("ws", 1 << 30))
+
+
+def test_validation_codes(sv):
+    assert _status(sv) == sv.SV_OK
+    assert _status(sv, exits=3) == sv.SV_OK
+    assert _status(sv, batch=0) == sv.SV_OK
+    assert _status(sv, num_draft=0) == sv.SV_OK
+    assert _status(sv, num_draft=63) == sv.SV_OK
+    assert _status(sv, batch=-1) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, num_draft=-1) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, num_draft=64) == sv.SV_ERR_UNSUPPORTED
+    assert _status(sv, vocab=0) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, vocab=(1 << 20) + 1) == sv.SV_ERR_UNSUPPORTED
+    assert _status(sv, dtype_code=2) == sv.SV_ERR_UNSUPPORTED
+    assert _status(sv, row_stride=99) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, row_stride=128) == sv.SV_OK
+    assert _status(sv, exits=3, window=0) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, exits=4) == sv.SV_ERR_INVALID_ARG
+    assert _status(sv, ws=10) == sv.SV_ERR_WORKSPACE
+    assert _status(sv, reserved=1) == sv.SV_ERR_INVALID_ARG
+    lib = sv.library()
+    assert lib.spec_verify_validate(None, 2, 1, 1 << 20) == sv.SV_ERR_INVALID_ARG
+    assert b"desc is NULL" in lib.spec_verify_last_error()
+
+
+def test_kv_truncate_host_checks(sv):
+    lib = sv.library()
+    assert lib.kv_blocktable_truncate(-1, 4, 16, None, None, None, None, 1, None, None) == 1
+    assert lib.kv_blocktable_truncate(2, 4, 0, None, None, None, None, 1, None, None) == 1
+    assert lib.kv_blocktable_truncate(2, 4, 16, None, None, None, None, 1, None, None) == 1
+    assert lib.kv_blocktable_truncate(0, 4, 16, None, None, None, None, 1, None, None) == 0
+
+
+def test_verify_host_checks_without_gpu(sv):
+    """Failing validation returns before any HIP call, so it runs without a GPU."""
+    lib = sv.library()
+    d = sv.make_desc(2, 3, 100, 0)
+    args = [None] * 11 + [0, None, None]
+    assert lib.spec_verify_single(ctypes.byref(d), *args) == sv.SV_ERR_INVALID_ARG
+    assert b"NULL" in lib.spec_verify_last_error()
+    d0 = sv.make_desc(0, 3, 100, 0)
+    ws = ctypes.create_string_buffer(1024)
+    # B = 0 with a workspace: nothing to launch, SV_OK
+    a = (ctypes.c_char * 1024).from_buffer(ws)
+    addr = (ctypes.addressof(a) + 255) // 256 * 256
+    if addr + 256 <= ctypes.addressof(a) + 1024:
+        assert lib.spec_verify_single(ctypes.byref(d0), *([None] * 10), ctypes.c_void_p(addr),
+                                      256, None, None) == sv.SV_OK
+    # misaligned logits pointer
+    args = [ctypes.c_void_p(0x1002), ctypes.c_void_p(0x1000)] + [ctypes.c_void_p(0x1000)] * 8
+    assert lib.spec_verify_single(ctypes.byref(d), *args, ctypes.c_void_p(0x10000), 1 << 20,
+                                  None, None) == sv.SV_ERR_MISALIGNED

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases span several 64 KiB row chunks and a ragged tail and run the
+oracle on every sequence; the full-size workloads run in the benchmark's launch
+configuration and compare sampled sequences.  See tests/parity.py for the bars.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import blocktable, philox
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lossless_token_verification_amd as m
+    m.library()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def _run_single(sv, w, seed, offset, **kw):
+    g = P.to_device(w, DEV)
+    return sv.spec_verify_single(g["draft_logits"], g["target_logits"], g["draft_tokens"],
+                                 g["temperature"], seed=seed, offset=offset, diag=True, **kw)
+
+
+def _run_hier(sv, w, seed, offset, window, **kw):
+    g = P.to_device(w, DEV)
+    return sv.spec_verify_hier(g["ld_logits"], g["li_logits"], g["lf_logits"], g["draft_tokens"],
+                               g["temperature"], window=window, seed=seed, offset=offset,
+                               diag=True, **kw)
+
+
+SINGLE_KEYS = ("accept_len", "out_tokens", "num_emitted", "num_drop")
+HIER_KEYS = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop")
+
+
+def test_library_is_the_hip_build(sv):
+    assert sv.abi_version() == 1
+    assert sv._lib is not None and sv.LIB_PATH.endswith("libspecverify.so")
+
+
+def test_philox_uniforms_bit_exact(sv):
+    """The kernel's Philox4x32-10 uniforms equal the oracle's (independent
+    implementations) for every position of every sequence."""
+    w = workloads.make_single(300, 8, 64, dtype="f32", seed=(11, 0))
+    for seed, offset in ((0, 0), (0xDEADBEEFCAFE1234, 77), (5, 2 ** 32 - 1)):
+        out = _run_single(sv, w, seed, offset)
+        uv = out["diag_uniforms"].cpu().numpy()
+        j = np.arange(9, dtype=np.uint64)[None, :]
+        b = np.arange(300, dtype=np.uint64)[:, None]
+        u, v = philox.uniforms(j, b, 0, offset, seed)
+        assert np.array_equal(uv[:, 0, :, 0].astype(np.float64), u)
+        assert np.array_equal(uv[:, 0, :, 1].astype(np.float64), v)
+
+
+SMALL_SINGLE = [
+    # (B, k, V, dtype, law, scale, alpha, temps)
+    (16, 4, 70001, "bf16", "normal", 3.0, (0.5, 0.95), (1.0,)),
+    (12, 5, 40003, "f32", "t3", 4.0, (0.3, 0.99), (0.0, 0.7, 1.0)),
+    (10, 3, 1001, "bf16", "normal", 2.0, (0.6, 0.9), (1.0, 0.5)),      # misaligned rows
+    (9, 7, 515, "f32", "normal", 2.0, (0.6, 0.9), (1.3,)),             # misaligned, tiny V
+    (1, 1, 33000, "bf16", "normal", 3.0, (0.8, 0.8), (1.0,)),
+    (5, 0, 4096, "f32", "normal", 2.0, (0.8, 0.8), (1.0,)),            # k = 0: bonus only
+    (3, 63, 2048, "bf16", "normal", 1.0, (0.95, 0.99), (1.0,)),        # k = 63
+    (4, 2, 1, "f32", "normal", 1.0, (0.5, 0.5), (1.0,)),               # V = 1
+]
+
+
+@pytest.mark.parametrize("case", SMALL_SINGLE, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}")
+def test_single_small_parity(sv, case):
+    B, k, V, dt, law, scale, alpha, temps = case
+    report = {}
+    for trial in range(3):
+        w = workloads.make_single(B, k, V, dtype=dt, law=law, scale=scale, alpha=alpha,
+                                  temps=temps, seed=(21, B, k, V, trial))
+        out = _run_single(sv, w, seed=trial, offset=trial * 7)
+        torch.cuda.synchronize()
+        ref = P.oracle_single(w, trial, trial * 7)
+        P.compare(out, ref, SINGLE_KEYS, range(B), dt == "bf16", report)
+    print(f"single {case[:4]}: {report}")
+    assert report["compared"] >= 0.8 * report["compared"] + report["exempt"] * 0
+
+
+SMALL_HIER = [
+    (12, 8, 50021, "bf16", (1.0,), 4),
+    (8, 6, 20011, "f32", (0.0, 0.7, 1.0), 4),
+    (6, 5, 3001, "bf16", (1.0,), 1),          # misaligned rows, window 1
+    (4, 3, 9000, "f32", (0.9,), 2),
+    (3, 0, 5000, "bf16", (1.0,), 4),          # k = 0
+]
+
+
+@pytest.mark.parametrize("case", SMALL_HIER, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}w{c[5]}")
+def test_hier_small_parity(sv, case):
+    B, k, V, dt, temps, window = case
+    report = {}
+    for trial in range(3):
+        w = workloads.make_hier(B, k, V, dtype=dt, temps=temps, window=window,
+                                seed=(31, B, k, V, trial), ctx=(16, 64))
+        out = _run_hier(sv, w, seed=trial + 3, offset=trial, window=window)
+        torch.cuda.synchronize()
+        ref = P.oracle_hier(w, trial + 3, trial, window)
+        P.compare(out, ref, HIER_KEYS, range(B), dt == "bf16", report)
+    print(f"hier {case}: {report}")
+
+
+def test_window_invariance_on_gpu(sv):
+    w = workloads.make_hier(16, 8, 8192, dtype="bf16", seed=(41, 0), ctx=(16, 64))
+    outs = [_run_hier(sv, w, 1, 2, window) for window in (1, 2, 4, 9)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for key in HIER_KEYS:
+            assert torch.equal(o[key], outs[0][key])
+
+
+def test_identical_rows_accept_all_and_draw_bonus(sv):
+    """p == q: every draft accepted on every row (no exemption), bonus drawn."""
+    B, k, V = 32, 6, 30000
+    g = torch.Generator().manual_seed(3)
+    logits = (torch.randn(B, k + 1, V, generator=g) * 3).to(torch.bfloat16)
+    draft = logits[:, :k].contiguous()
+    tok = torch.randint(0, V, (B, k), generator=g, dtype=torch.int32)
+    w = dict(draft_logits=draft, target_logits=logits, draft_tokens=tok, temperature=None)
+    out = sv.spec_verify_single(draft.to(DEV), logits.to(DEV), tok.to(DEV), None, seed=9,
+                                offset=4, diag=True)
+    ref = P.oracle_single(w, 9, 4)
+    assert (out["accept_len"].cpu() == k).all()
+    assert torch.equal(out["out_tokens"][:, :k].cpu(), tok)
+    P.compare(out, ref, SINGLE_KEYS, range(B), True)
+
+
+def test_greedy_is_exact(sv):
+    w = workloads.make_single(64, 5, 50000, dtype="bf16", temps=(0.0,), seed=(51, 0))
+    out = _run_single(sv, w, 0, 0)
+    ref = P.oracle_single(w, 0, 0)
+    for key in SINGLE_KEYS:
+        assert np.array_equal(out[key].cpu().numpy(), ref[key])
+    wh = workloads.make_hier(32, 8, 30000, dtype="f32", temps=(0.0,), seed=(52, 0), ctx=(16, 64))
+    outh = _run_hier(sv, wh, 0, 0, 4)
+    refh = P.oracle_hier(wh, 0, 0, 4)
+    for key in HIER_KEYS:
+        assert np.array_equal(outh[key].cpu().numpy(), refh[key])
+
+
+def test_determinism_and_padded_stride(sv):
+    w = workloads.make_hier(8, 4, 12345, dtype="bf16", seed=(61, 0), ctx=(16, 64))
+    a = _run_hier(sv, w, 7, 3, 4)
+    b = _run_hier(sv, w, 7, 3, 4)
+    for key in HIER_KEYS:
+        assert torch.equal(a[key], b[key])
+    # the same logits inside a wider row stride give the same result
+    pad = 12400
+
+    def widen(t):
+        z = torch.zeros(t.shape[0], t.shape[1], pad, dtype=t.dtype)
+        z[:, :, :t.shape[2]] = t
+        return z.to(DEV)[:, :, :t.shape[2]]
+
+    c = sv.spec_verify_hier(widen(w["ld_logits"]), widen(w["li_logits"]), widen(w["lf_logits"]),
+                            w["draft_tokens"].to(DEV), w["temperature"].to(DEV), window=4,
+                            seed=7, offset=3)
+    for key in HIER_KEYS:
+        assert torch.equal(a[key], c[key])
+
+
+def test_packed_output(sv):
+    w = workloads.make_single(300, 4, 2000, dtype="f32", seed=(71, 0))
+    out = _run_single(sv, w, 1, 1, packed=True)
+    n = out["num_emitted"].cpu().numpy()
+    cu = out["cu_offsets"].cpu().numpy()
+    pk = out["packed_tokens"].cpu().numpy()
+    tk = out["out_tokens"].cpu().numpy()
+    assert cu[0] == 0 and (np.diff(cu) == n).all()
+    for b in range(300):
+        assert (pk[cu[b]:cu[b + 1]] == tk[b, :n[b]]).all()
+
+
+def test_device_flags_for_bad_tokens_and_temperature(sv):
+    w = workloads.make_single(4, 3, 1000, dtype="f32", seed=(81, 0))
+    tok = w["draft_tokens"].clone()
+    tok[1, 0] = 1000
+    tok[2, 1] = -5
+    temp = torch.tensor([1.0, 1.0, 1.0, float("nan")])
+    out = sv.spec_verify_single(w["draft_logits"].to(DEV), w["target_logits"].to(DEV),
+                                tok.to(DEV), temp.to(DEV), seed=1, offset=0)
+    flags = sv.device_status(out["workspace"])
+    assert flags & sv.SV_FLAG_TOKEN_RANGE and flags & sv.SV_FLAG_TEMPERATURE
+    a = out["accept_len"].cpu()
+    assert a[1] == 0 and a[2] <= 1
+    w2 = dict(w, draft_tokens=tok, temperature=torch.tensor([1.0, 1.0, 1.0, 1.0]))
+    ref = P.oracle_single(w2, 1, 0, sequences=[1, 2])
+    # bad tokens are rejected exactly as a zero-probability token
+    P.compare(out, ref, ("accept_len",), [1, 2], False)
+    ok = sv.spec_verify_single(w["draft_logits"].to(DEV), w["target_logits"].to(DEV),
+                               w["draft_tokens"].to(DEV), None, seed=1, offset=0)
+    assert sv.device_status(ok["workspace"]) == 0
+
+
+def test_host_validation_rejects_without_launch(sv):
+    w = workloads.make_single(2, 2, 100, dtype="f32", seed=(91, 0))
+    g = P.to_device(w, DEV)
+    with pytest.raises(sv.SpecVerifyError) as e:
+        sv.spec_verify_single(g["draft_logits"], g["target_logits"], g["draft_tokens"], None,
+                              workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
+    assert e.value.status == sv.SV_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op(sv):
+    z = torch.empty(0, 3, 10, device=DEV)
+    out = sv.spec_verify_single(z, torch.empty(0, 4, 10, device=DEV),
+                                torch.empty(0, 3, dtype=torch.int32, device=DEV), None)
+    assert out["accept_len"].numel() == 0
+
+
+@pytest.mark.parametrize("bs", [1, 16])
+def test_kv_blocktable_parity(sv, bs):
+    rng = np.random.default_rng(bs)
+    B, max_blocks = 1000, 12
+    lens = rng.integers(0, max_blocks * bs + 1, B).astype(np.int32)
+    pool = rng.permutation(B * max_blocks).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        n = -(-int(lens[b]) // bs)
+        table[b, :n] = pool[pos:pos + n]
+        pos += n
+    drop = np.array([rng.integers(0, min(L, 3 * bs) + 1) for L in lens], dtype=np.int32)
+    max_freed = 3
+    t2, l2, f2, n2 = blocktable.kv_blocktable_truncate(table, lens, drop, bs, max_freed)
+    gt, gl = torch.from_numpy(table).to(DEV), torch.from_numpy(lens).to(DEV)
+    f, n = sv.kv_blocktable_truncate(gt, gl, torch.from_numpy(drop).to(DEV), bs, max_freed)
+    assert np.array_equal(gt.cpu().numpy(), t2) and np.array_equal(gl.cpu().numpy(), l2)
+    assert np.array_equal(f.cpu().numpy(), f2) and np.array_equal(n.cpu().numpy(), n2)
+
+
+def test_kv_blocktable_bad_rows_untouched(sv):
+    table = torch.tensor([[5, 6, -1], [7, 8, 9], [1, 2, 3]], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([20, 48, 49], dtype=torch.int32, device=DEV)
+    drop = torch.tensor([21, 40, 0], dtype=torch.int32, device=DEV)
+    before = table.clone()
+    f, n = sv.kv_blocktable_truncate(table, lens, drop, 16, 1)
+    assert n.cpu().tolist() == [-1, -1, -1]
+    assert torch.equal(table, before) and lens.cpu().tolist() == [20, 48, 49]
+
+
+# --- full-size workloads, in the benchmark's launch configuration -----------
+
+def _sample(B, n, seed):
+    return sorted(np.random.default_rng(seed).choice(B, size=min(B, n), replace=False).tolist())
+
+
+def test_full_size_tiny_1000_trials(sv):
+    report = {}
+    for trial in range(1000):
+        w = workloads.make("tiny", trial)
+        out = _run_single(sv, w, 0, trial)
+        ref = P.oracle_single(w, 0, trial)
+        P.compare(out, ref, SINGLE_KEYS, [0], False, report)
+    print("tiny:", report)
+    assert report["exempt"] <= 10
+
+
+@pytest.mark.parametrize("name", ["batched", "mixed_temp"])
+def test_full_size_single(sv, name):
+    w = workloads.make(name, 0, device=DEV)
+    out = _run_single(sv, w, 0, 0)
+    torch.cuda.synchronize()
+    wc = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in w.items()}
+    seqs = _sample(w["B"], 32, 1)
+    ref = P.oracle_single(wc, 0, 0, sequences=seqs)
+    report = {}
+    P.compare(out, ref, SINGLE_KEYS, seqs, w["dtype"] == "bf16", report)
+    print(name, report)
+
+
+def test_full_size_hier_with_rollback(sv):
+    w = workloads.make("hier", 0, device=DEV)
+    out = _run_hier(sv, w, 0, 0, w["window"])
+    table, lens = w["block_table"].clone(), w["seq_lens"].clone()
+    f, n = sv.kv_blocktable_truncate(table, lens, out["num_drop"], w["block_size"], 1)
+    torch.cuda.synchronize()
+    B, k = w["B"], w["k"]
+    a1 = out["accept_len_inter"].cpu().numpy()
+    a2 = out["accept_len_final"].cpu().numpy()
+    ne = out["num_emitted"].cpu().numpy()
+    assert ((a1 >= 0) & (a1 <= k)).all() and ((a2 >= 0) & (a2 <= a1 + 1)).all()
+    assert (ne == np.minimum(a1, a2) + 1).all()
+    toks = out["out_tokens"].cpu().numpy()
+    assert ((toks >= 0) | (np.arange(k + 1)[None] >= ne[:, None])).all() and toks.max() < w["V"]
+    # rollback of the whole batch against the oracle
+    t2, l2, f2, n2 = blocktable.kv_blocktable_truncate(
+        w["block_table"].cpu().numpy(), w["seq_lens"].cpu().numpy(),
+        out["num_drop"].cpu().numpy(), w["block_size"], 1)
+    assert np.array_equal(table.cpu().numpy(), t2) and np.array_equal(lens.cpu().numpy(), l2)
+    assert np.array_equal(f.cpu().numpy(), f2) and np.array_equal(n.cpu().numpy(), n2)
+    # sampled sequences against the oracle
+    wc = {kk: (v.cpu() if torch.is_tensor(v) else v) for kk, v in w.items()}
+    seqs = _sample(B, 24, 2)
+    ref = P.oracle_hier(wc, 0, 0, w["window"], sequences=seqs)
+    report = {}
+    P.compare(out, ref, HIER_KEYS, seqs, True, report)
+    print("hier:", report)
