@@ -78,9 +78,9 @@ def verify_chain(Q_rows, P_rows, tokens, us, vs, bonus_row=None, window=None):
       info    per tested position (u, p, q) and the draw info (or None).
     """
     n = len(tokens)
-    w = n if window is None else int(window)
-    if w < 1:
+    if window is not None and int(window) < 1:
         raise ValueError("window must be >= 1")
+    w = max(n, 1) if window is None else int(window)
     tests = []
     a = n
     start = 0

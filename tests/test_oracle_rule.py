@@ -199,3 +199,11 @@ def test_fraction_and_float_paths_agree():
         r2 = rule.verify_chain(Qx, Px[:k], x, [Fraction(u) for u in us],
                                [Fraction(v) for v in vs], bonus_row=Px[k])
         assert r1[0] == r2[0] and r1[1] == r2[1]
+
+
+def test_no_drafts_draws_the_bonus():
+    """k = 0: nothing to verify, the bonus token is drawn from P_0."""
+    P0 = np.array([0.1, 0.6, 0.3])
+    for v, want in ((0.05, 0), (0.1, 1), (0.69, 1), (0.7, 2), (0.999, 2)):
+        a, emitted, _ = rule.verify_chain([], [], [], [0.5], [v], bonus_row=P0)
+        assert a == 0 and emitted == [want]
