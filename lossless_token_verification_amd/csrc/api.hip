@@ -1,7 +1,9 @@
 // C ABI of libspecverify.so: host-side validation, workspace layout and the
 // launch sequence of each call.  See include/spec_verify.h for the contract.
+#include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -25,6 +27,7 @@ struct Plan {
   int nc = 0;
   int64_t ld = 0;
   size_t ws_bytes = 0;
+  size_t seq_bytes = 0;   // per-sequence counters and stage-1 results
   int32_t exit_pos[3] = {0, 0, 0};
   int32_t exit_row0[3] = {0, 0, 0};
 };
@@ -64,7 +67,9 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   if (p->rows_total > INT32_MAX || p->rows_total * p->nc > INT32_MAX)
     return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
   p->ld = ld;
-  p->ws_bytes = sv::kFlagsBytes + static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
+  p->seq_bytes = (static_cast<size_t>(B) * 4 * sizeof(int32_t) + 255) / 256 * 256;
+  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes +
+                static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
   return SV_OK;
 }
 
@@ -100,6 +105,17 @@ int32_t check_diag(const spec_verify_diag* diag) {
   if (diag->draws && !aligned_to(diag->draws, 8))
     return fail(SV_ERR_MISALIGNED, "diag.draws not 8-byte aligned");
   return SV_OK;
+}
+
+// Sequences between a sequence's stage-1 rows and its L_f rows in the launch
+// order (tuning knob; SPEC_VERIFY_LAG overrides it).
+int lag_sequences() {
+  static const int lag = [] {
+    const char* env = std::getenv("SPEC_VERIFY_LAG");
+    const int v = env ? std::atoi(env) : sv::kLagSeqs;
+    return v < 0 ? 0 : v;
+  }();
+  return lag;
 }
 
 int32_t device_error(hipError_t e, const char* what) {
@@ -141,66 +157,62 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   if (!any) return SV_OK;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  uint32_t* flags = static_cast<uint32_t*>(workspace);
-  sv::Partial* partials =
-      reinterpret_cast<sv::Partial*>(static_cast<char*>(workspace) + sv::kFlagsBytes);
-
-  sv::RowStatsArgs ra{};
-  for (int e = 0; e < 3; ++e) {
-    ra.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
-    ra.exit_pos[e] = p.exit_pos[e];
-    ra.exit_row0[e] = e < num_exits ? p.exit_row0[e] : INT32_MAX;
-  }
-  ra.num_exits = num_exits;
-  ra.V = desc->vocab;
-  ra.ld = p.ld;
-  ra.nc = p.nc;
-  ra.dtype = desc->dtype;
-  ra.temperature = temperature;
-  ra.partials = partials;
-  ra.flags = flags;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
+  int32_t* seqw = reinterpret_cast<int32_t*>(ws + sv::kFlagsBytes);
+  sv::Partial* partials = reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes);
+  const int B = desc->batch;
   hipError_t err;
+
+  // counters (cnt1, cnt2) and the flags start at zero
+  sv::ClearArgs ca{2 * B, seqw, flags};
+  err = sv::launch_clear(ca, st);
+  if (err != hipSuccess) return device_error(err, "clear launch");
+
+  sv::FusedArgs fa{};
+  fa.hier = num_exits == 3;
+  fa.B = B;
+  fa.k = desc->num_draft;
+  fa.V = desc->vocab;
+  fa.dtype = desc->dtype;
+  fa.nc = p.nc;
+  fa.window = num_exits == 3 ? window : 1;
+  fa.ld = p.ld;
+  for (int e = 0; e < 3; ++e) {
+    fa.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+    fa.exit_row0[e] = e < num_exits ? p.exit_row0[e] : 0;
+  }
+  fa.n1 = (2 * fa.k + 1) * p.nc;
+  fa.n2 = num_exits == 3 ? (fa.k + 1) * p.nc : 0;
+  fa.lag = num_exits == 3 ? std::min(B, lag_sequences()) : 0;
+  fa.partials = partials;
+  fa.cnt1 = seqw;
+  fa.cnt2 = seqw + B;
+  fa.st1 = seqw + 2 * B;
+  fa.tokens = tokens;
+  fa.temperature = temperature;
+  fa.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  fa.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  fa.offset = desc->offset;
+  fa.accept_len = accept_len;
+  fa.accept_len_final = num_exits == 3 ? accept_len_final : nullptr;
+  fa.out_tokens = out_tokens;
+  fa.num_emitted = num_emitted;
+  fa.num_drop = num_drop;
+  fa.diag_uniforms = diag ? diag->uniforms : nullptr;
+  fa.diag_probs = diag ? diag->probs : nullptr;
+  fa.diag_draws = diag ? diag->draws : nullptr;
+  fa.flags = flags;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
     if (err != hipSuccess) return device_error(err, "event record");
   }
-  err = sv::launch_rowstats(ra, static_cast<int>(p.rows_total), st);
-  if (err != hipSuccess) return device_error(err, "row statistics launch");
+  err = sv::launch_fused(fa, p.rows_total * p.nc, st);
+  if (err != hipSuccess) return device_error(err, "verify launch");
   if (diag && diag->stats_end) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
     if (err != hipSuccess) return device_error(err, "event record");
   }
-
-  sv::VerifyArgs va{};
-  va.hier = num_exits == 3;
-  va.B = desc->batch;
-  va.k = desc->num_draft;
-  va.V = desc->vocab;
-  va.dtype = desc->dtype;
-  va.nc = p.nc;
-  va.window = num_exits == 3 ? window : 1;
-  va.ld = p.ld;
-  for (int e = 0; e < 3; ++e) {
-    va.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
-    va.exit_row0[e] = e < num_exits ? p.exit_row0[e] : 0;
-  }
-  va.partials = partials;
-  va.tokens = tokens;
-  va.temperature = temperature;
-  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
-  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
-  va.offset = desc->offset;
-  va.accept_len = accept_len;
-  va.accept_len_final = num_exits == 3 ? accept_len_final : nullptr;
-  va.out_tokens = out_tokens;
-  va.num_emitted = num_emitted;
-  va.num_drop = num_drop;
-  va.diag_uniforms = diag ? diag->uniforms : nullptr;
-  va.diag_probs = diag ? diag->probs : nullptr;
-  va.diag_draws = diag ? diag->draws : nullptr;
-  va.flags = flags;
-  err = sv::launch_verify(va, st);
-  if (err != hipSuccess) return device_error(err, "verify launch");
 
   if (packed) {
     sv::PackArgs pa{desc->batch, desc->num_draft, out_tokens, num_emitted, packed, cu_offsets};

@@ -43,30 +43,26 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 16, "Partial layout");
 
-// Workspace: [flags (256 B)] [partials: rows_total * nc]
+// Workspace: [flags (256 B)] [cnt1, cnt2, st1: 4 int32 per sequence, padded
+// to 256 B] [partials: rows_total * nc]
 constexpr size_t kFlagsBytes = 256;
+constexpr int kLagSeqs = 32;
 
-struct RowStatsArgs {
-  const void* exit_ptr[3];
-  int32_t exit_pos[3];   // rows per sequence in each exit (k or k + 1)
-  int32_t exit_row0[3];  // first global row id of each exit
-  int32_t num_exits;
-  int32_t V;
-  int64_t ld;            // row stride in elements
-  int32_t nc;            // chunks per row
-  int32_t dtype;
-  const float* temperature;
-  Partial* partials;
-  uint32_t* flags;
-};
-
-struct VerifyArgs {
-  int32_t hier;          // 0: single stage (q = exit 0, p = exit 1); 1: L_d, L_i, L_f
+// One launch of the fused kernel: the HBM stream of row statistics plus, for
+// each sequence, the verification run by the workgroup that completes its
+// statistics.
+struct FusedArgs {
+  int32_t hier;            // 0: single stage (q = exit 0, p = exit 1); 1: L_d, L_i, L_f
   int32_t B, k, V, dtype, nc, window;
-  int64_t ld;
+  int64_t ld;              // row stride in elements
   const void* exit_ptr[3];
-  int32_t exit_row0[3];
-  const Partial* partials;
+  int32_t exit_row0[3];    // first global row id of each exit (partials layout)
+  int32_t n1, n2;          // workgroups per sequence: stage-1 rows, L_f rows
+  int32_t lag;             // L_f rows of sequence b follow stage-1 rows of b + lag
+  Partial* partials;       // [rows_total * nc]
+  int32_t* cnt1;           // [B] stage-1 chunks done
+  int32_t* cnt2;           // [B] L_f chunks done + 1 when stage 1 is done
+  int32_t* st1;            // [B, 2] stage-1 result (a1, correction or bonus token)
   const int32_t* tokens;
   const float* temperature;
   uint32_t key0, key1, offset;
@@ -78,6 +74,12 @@ struct VerifyArgs {
   float* diag_uniforms;
   double* diag_probs;
   double* diag_draws;
+  uint32_t* flags;
+};
+
+struct ClearArgs {
+  int32_t n;
+  int32_t* words;          // n int32 set to 0
   uint32_t* flags;
 };
 
@@ -98,8 +100,8 @@ struct KvArgs {
   int32_t* num_freed;
 };
 
-hipError_t launch_rowstats(const RowStatsArgs& a, int rows_total, hipStream_t st);
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_clear(const ClearArgs& a, hipStream_t st);
+hipError_t launch_fused(const FusedArgs& a, int64_t items, hipStream_t st);
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_kv_truncate(const KvArgs& a, hipStream_t st);
 

@@ -1,20 +1,20 @@
-// Row statistics: the HBM stream of the verification path.
+// Chunk statistics: the HBM stream of the verification path.
 //
 // Every logit row of every exit (draft / target, or L_d / L_i / L_f) is read
-// once.  One workgroup handles one 64 KiB chunk of one row: each thread issues
-// its 16 nontemporal 128-bit loads up front, keeps the chunk in registers, and
-// reduces it to partial softmax statistics:
+// once, in 64 KiB chunks.  Each of the 256 threads of a workgroup issues its 16
+// nontemporal 128-bit loads up front, keeps the chunk in registers and reduces
+// it to partial softmax statistics:
 //   temperature > 0: c = round(max * s) and S = sum 2^(l * s - c), with
 //                    s = log2(e) / temperature (fp32 exponent, fp64 sum);
 //   temperature = 0: the maximum and its lowest index (greedy decoding).
-// The verify kernel merges the chunks of the rows it needs.  Softmax of a row
-// is the per-exit token distribution the rule compares ("Kernmechanismus" of
-// the HiSpec summary: the exits L_d, L_i, L_f each yield a token distribution).
+// The softmax of a row is the token distribution of that exit at that position
+// (HiSpec summary, section 2 "Kernmechanismus": L_d, L_i and L_f each yield a
+// token distribution).
+#pragma once
+
 #include "sv_common.h"
 
 namespace sv {
-
-namespace {
 
 struct Red {
   float key;
@@ -23,7 +23,7 @@ struct Red {
 };
 
 // Workgroup reduction of greedy (max, lowest index) pairs.
-__device__ void block_argmax(float& m, int& idx, Red* lds) {
+__device__ inline void block_argmax(float& m, int& idx, Red* lds) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -52,7 +52,7 @@ __device__ void block_argmax(float& m, int& idx, Red* lds) {
 
 // Workgroup reduction of (c, S) partial sums: common reference max(c), then
 // each S rescaled by 2^(c_t - c) in double and summed.
-__device__ void block_logsum(float& c, double& S, Red* lds) {
+__device__ inline void block_logsum(float& c, double& S, Red* lds) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   float cm = wave_max(c);
   if (lane == 0) lds[wave].key = cm;
@@ -85,30 +85,12 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 
   }
 }
 
+// Partial statistics of elements [e0, e1) of one row (e1 - e0 <= one chunk).
+// Called by the whole workgroup (it contains barriers).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
+__device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds) {
   constexpr int VPE = DT == 1 ? 8 : 4;
-  constexpr int ES = DT == 1 ? 2 : 4;
-  constexpr int CE = kChunkBytes / ES;
-  __shared__ Red lds[kWaves];
-
-  const int row = blockIdx.x / a.nc;
-  const int chunk = blockIdx.x - row * a.nc;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0) a.flags[0] = 0u;  // flags of this call start clear
-
-  int e = 0;
-  if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
-  if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
-  const int local = row - a.exit_row0[e];
-  const int b = local / a.exit_pos[e];
-  const float tau = a.temperature ? a.temperature[b] : 1.0f;
-  const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
-  const float s = greedy ? 0.0f : kLog2e / tau;
-  const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
-  const int e0 = chunk * CE;
-  const int e1 = min(a.V, e0 + CE);
-
   float m = -INFINITY;
   int idx = 0x7fffffff;
   double S = 0.0;
@@ -142,6 +124,10 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
     }
     m = fmaxf(fmaxf(m0, m1), xt);
     const bool empty = !(m > -INFINITY);   // no finite element in this thread's share
+    // Decode again below instead of keeping 8 decoded floats per vector live
+    // (that would double the registers and halve the waves per SIMD).
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) asm volatile("" : "+v"(buf[i]));
 
     if (greedy) {
       // lowest index attaining the thread's maximum
@@ -212,18 +198,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
     out.amax = -1;
     out.S = S;
   }
-  if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = out;
-}
-
-}  // namespace
-
-hipError_t launch_rowstats(const RowStatsArgs& a, int rows_total, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(rows_total) * static_cast<unsigned>(a.nc));
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(rowstats_kernel<1>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(rowstats_kernel<0>, grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return out;
 }
 
 }  // namespace sv

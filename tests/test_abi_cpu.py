@@ -48,10 +48,13 @@ def test_version_and_status_strings(sv):
 
 
 def test_workspace_size_formula(sv):
-    # 256 B of flags + one 16-byte partial per (row, 64 KiB chunk)
-    assert sv.workspace_bytes(256, 8, 128256, 1, 3) == 256 + 256 * 26 * 4 * 16
-    assert sv.workspace_bytes(64, 4, 32000, 1, 2) == 256 + 64 * 9 * 1 * 16
-    assert sv.workspace_bytes(32, 5, 151936, 0, 2) == 256 + 32 * 11 * 10 * 16
+    # 256 B of flags + 16 B per sequence (padded to 256) + one 16-byte partial
+    # per (row, 64 KiB chunk)
+    def pad(n):
+        return (n + 255) // 256 * 256
+    assert sv.workspace_bytes(256, 8, 128256, 1, 3) == 256 + pad(256 * 16) + 256 * 26 * 4 * 16
+    assert sv.workspace_bytes(64, 4, 32000, 1, 2) == 256 + pad(64 * 16) + 64 * 9 * 1 * 16
+    assert sv.workspace_bytes(32, 5, 151936, 0, 2) == 256 + pad(32 * 16) + 32 * 11 * 10 * 16
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 
