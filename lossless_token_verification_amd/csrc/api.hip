@@ -188,7 +188,7 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   fa.partials = partials;
   fa.cnt1 = seqw;
   fa.cnt2 = seqw + B;
-  fa.st1 = seqw + 2 * B;
+  fa.st1 = reinterpret_cast<uint64_t*>(seqw + 2 * B);
   fa.tokens = tokens;
   fa.temperature = temperature;
   fa.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);

@@ -78,19 +78,15 @@ void fused_kernel(FusedArgs a) {
   const Partial p = chunk_stats<DT>(rowp, e0, min(a.V, e0 + CE), greedy, s, sm.red);
 
   if (tid == 0) {
-    a.partials[(a.exit_row0[e] + row_local) * a.nc + c] = p;
-    __threadfence();
+    publish_partial(a.partials + (a.exit_row0[e] + row_local) * a.nc + c, p);
     const int old = atomicAdd(it.f ? &a.cnt2[b] : &a.cnt1[b], 1);
     is_last = it.f ? (old == a.n2) : (old == a.n1 - 1);
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();   // the other workgroups' partials are visible from here on
+  // every partial of this sequence's rows has been published
   bool stage2 = it.f != 0;
-  if (!stage2) {
-    stage2 = verify_stage1<DT>(a, b, sm.v);
-    if (stage2) __threadfence();
-  }
+  if (!stage2) stage2 = verify_stage1<DT>(a, b, sm.v);
   if (stage2) verify_stage2<DT>(a, b, sm.v);
 }
 

@@ -62,7 +62,7 @@ struct FusedArgs {
   Partial* partials;       // [rows_total * nc]
   int32_t* cnt1;           // [B] stage-1 chunks done
   int32_t* cnt2;           // [B] L_f chunks done + 1 when stage 1 is done
-  int32_t* st1;            // [B, 2] stage-1 result (a1, correction or bonus token)
+  uint64_t* st1;           // [B] stage-1 result: a1 | (correction or bonus token) << 32
   const int32_t* tokens;
   const float* temperature;
   uint32_t key0, key1, offset;
@@ -107,6 +107,34 @@ hipError_t launch_kv_truncate(const KvArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // device helpers
+
+// Publication of per-sequence data between workgroups without cache-wide
+// fences: writers swap the words in with device-scope atomics and wait for the
+// swaps to return before counting themselves done; readers load them with
+// device-scope atomic loads, which read the coherent copy.
+__device__ __forceinline__ void publish_u64(uint64_t* p, uint64_t v) {
+  const unsigned long long old = atomicExch(reinterpret_cast<unsigned long long*>(p),
+                                            static_cast<unsigned long long>(v));
+  asm volatile("" ::"v"(old));   // the swap has completed before anything later is issued
+}
+__device__ __forceinline__ uint64_t fetch_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_partial(Partial* dst, const Partial& v) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(dst);
+  publish_u64(w, static_cast<uint64_t>(__float_as_uint(v.key)) |
+                     (static_cast<uint64_t>(static_cast<uint32_t>(v.amax)) << 32));
+  publish_u64(w + 1, static_cast<uint64_t>(__double_as_longlong(v.S)));
+}
+__device__ __forceinline__ Partial fetch_partial(const Partial* src) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(src);
+  const uint64_t a = fetch_u64(w), b = fetch_u64(w + 1);
+  Partial r;
+  r.key = __uint_as_float(static_cast<uint32_t>(a));
+  r.amax = static_cast<int32_t>(static_cast<uint32_t>(a >> 32));
+  r.S = __longlong_as_double(static_cast<long long>(b));
+  return r;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -306,7 +306,7 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool gre
     r.key = -INFINITY;
     r.amax = 0x7fffffff;
     for (int c = 0; c < nc; ++c) {
-      const Partial q = pp[c];
+      const Partial q = fetch_partial(pp + c);
       if (q.key > r.key || (q.key == r.key && q.amax < r.amax)) {
         r.key = q.key;
         r.amax = q.amax;
@@ -315,11 +315,12 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool gre
     r.S = 0.0;
     r.inv_S = 0.0f;
   } else {
+    // the reference of the whole row first, then the rescaled sums
     float cm = -INFINITY;
-    for (int c = 0; c < nc; ++c) cm = fmaxf(cm, pp[c].key);
+    for (int c = 0; c < nc; ++c) cm = fmaxf(cm, fetch_partial(pp + c).key);
     double S = 0.0;
     for (int c = 0; c < nc; ++c) {
-      const Partial q = pp[c];
+      const Partial q = fetch_partial(pp + c);
       if (q.S > 0.0) S += q.S * exp2(static_cast<double>(q.key) - static_cast<double>(cm));
     }
     r.key = cm;
@@ -516,9 +517,8 @@ __device__ bool verify_stage1(const FusedArgs& a, int b, VerifyShared& sm) {
   __shared__ int last;
   if (tid == 0) {
     a.accept_len[b] = a1;
-    a.st1[2 * b] = a1;
-    a.st1[2 * b + 1] = y;
-    __threadfence();
+    publish_u64(a.st1 + b, static_cast<uint64_t>(static_cast<uint32_t>(a1)) |
+                               (static_cast<uint64_t>(static_cast<uint32_t>(y)) << 32));
     const int old = atomicAdd(&a.cnt2[b], 1);
     last = (old == a.n2);
   }
@@ -531,8 +531,9 @@ template <int DT>
 __device__ void verify_stage2(const FusedArgs& a, int b, VerifyShared& sm) {
   SeqCtx<DT> cx(a, sm, b);
   const int tid = threadIdx.x, k = a.k;
-  const int a1 = a.st1[2 * b];
-  const int y = a.st1[2 * b + 1];
+  const uint64_t r1 = fetch_u64(a.st1 + b);
+  const int a1 = static_cast<int>(static_cast<uint32_t>(r1));
+  const int y = static_cast<int>(static_cast<uint32_t>(r1 >> 32));
   const int n2 = a1 + 1;
   if (tid < a1) sm.toks[tid] = a.tokens[static_cast<int64_t>(b) * k + tid];
   if (tid == a1) sm.toks[tid] = y;
