@@ -2,9 +2,9 @@
 
 A step is one pass of the whole path over one batch of the hierarchical
 workload (B=256 sequences, k=8 drafted tokens, V=128256, bf16 logits of the
-three exits L_d, L_i, L_f, windows of N_i=4): spec_verify_hier (row statistics
-of every logit row, both verification stages, correction draws) followed by
-kv_blocktable_truncate on the batch's paged-KV state.  Inputs are synthetic
+three exits L_d, L_i, L_f, windows of N_i=4): spec_verify_hier_rollback (row
+statistics of every logit row, both verification stages, correction draws,
+and the rollback of the batch's paged-KV block tables).  Inputs are synthetic
 (seeded, see workloads/) and resident in HBM before the timed region.
 
 Prints one JSON line: verified draft tokens/s (B*k per step), whole-step and
@@ -110,8 +110,8 @@ def _traffic(launch_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -145,14 +145,19 @@ def main():
 
     ev = HipEvents(2 * args.steps + 2)
 
+    bufs = {}
+
     def step(i, events=None):
-        out = sv.spec_verify_hier(w["ld_logits"], w["li_logits"], w["lf_logits"],
-                                  w["draft_tokens"], w["temperature"], window=w["window"],
-                                  seed=0, offset=i, workspace=ws, events=events)
-        sv.kv_blocktable_truncate(table, lens, out["num_drop"], w["block_size"], 1)
-        return out
+        # verification of both stages and the paged-KV rollback, one call
+        return sv.spec_verify_hier_rollback(w["ld_logits"], w["li_logits"], w["lf_logits"],
+                                            w["draft_tokens"], w["temperature"], table, lens,
+                                            block_size=w["block_size"], max_freed=1,
+                                            window=w["window"], seed=0, offset=i,
+                                            workspace=ws, events=events,
+                                            out=bufs.get("out"))
 
     table, lens = table0.clone(), lens0.clone()
+    bufs["out"] = step(999999)
     for i in range(args.warmup):
         step(1000000 + i)
     torch.cuda.synchronize()
@@ -162,8 +167,10 @@ def main():
     hip = ev.hip
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     hip.hipEventRecord(ev.ev[-2], stream)
+    t_host = time.perf_counter()
     for i in range(args.steps):
         step(i, events=(ev.ev[2 * i].value, ev.ev[2 * i + 1].value))
+    t_host = time.perf_counter() - t_host
     hip.hipEventRecord(ev.ev[-1], stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(2 * args.steps, 2 * args.steps + 1)
@@ -193,6 +200,7 @@ def main():
                                "logits of L_d/L_i/L_f, window N_i=4, 16-slot KV blocks",
                    "B": B, "k": k, "V": V, "logits": "bf16", "window": w["window"],
                    "block_size": w["block_size"]},
+        "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_of_peak_step": round(step_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "rowstats_kernel<bf16>",

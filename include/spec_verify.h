@@ -213,6 +213,23 @@ int32_t kv_blocktable_truncate(int32_t batch, int32_t max_blocks, int32_t block_
                                const int32_t* num_drop, int32_t* freed_blocks,
                                int32_t max_freed, int32_t* num_freed, void* hip_stream);
 
+/* spec_verify_hier followed by kv_blocktable_truncate with its num_drop, in the
+ * same launches: each sequence's paged-KV state is rolled back as soon as its
+ * result is known (HiSpec summary section 2: entries of discarded tokens are
+ * removed before the next phase, per-sequence lengths without padding).
+ * Arguments as for the two calls; num_drop may be NULL; the rollback's
+ * num_drop is the call's own.  A workspace sized for spec_verify_hier. */
+int32_t spec_verify_hier_rollback(const spec_verify_desc* desc, int32_t window,
+                                  const void* ld_logits, const void* li_logits,
+                                  const void* lf_logits, const int32_t* draft_tokens,
+                                  const float* temperature, int32_t* accept_len_inter,
+                                  int32_t* accept_len_final, int32_t* out_tokens,
+                                  int32_t* num_emitted, int32_t* num_drop, int32_t max_blocks,
+                                  int32_t block_size, int32_t* block_table, int32_t* seq_lens,
+                                  int32_t* freed_blocks, int32_t max_freed, int32_t* num_freed,
+                                  void* workspace, size_t workspace_bytes,
+                                  const spec_verify_diag* diag, void* hip_stream);
+
 /* Synchronises hip_stream, then copies the device flags (SV_FLAG_*) of the
  * last verify call that used `workspace` into *flags_out (host). */
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream);

@@ -12,6 +12,7 @@ Functions mirror the C entry points:
 * ``spec_verify_single``  -- standard rule, draft vs target (+ bonus token);
 * ``spec_verify_hier``    -- HiSpec two-stage L_d -> L_i -> L_f verification;
 * ``kv_blocktable_truncate`` -- paged-KV rollback of rejected drafted slots;
+* ``spec_verify_hier_rollback`` -- the two above in the same launches;
 * ``workspace_bytes``, ``validate``, ``device_status``, ``abi_version``.
 """
 
@@ -40,7 +41,8 @@ MAX_VOCAB = 1 << 20
 EXPORTED = (
     "spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
     "spec_verify_workspace_bytes", "spec_verify_validate", "spec_verify_single",
-    "spec_verify_hier", "kv_blocktable_truncate", "spec_verify_device_status",
+    "spec_verify_hier", "kv_blocktable_truncate", "spec_verify_hier_rollback",
+    "spec_verify_device_status",
 )
 
 
@@ -91,6 +93,10 @@ def library():
     lib.spec_verify_hier.restype = i32
     lib.spec_verify_hier.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P, P, P, P, P, P,
                                      P, P, sz, ctypes.POINTER(Diag), P]
+    lib.spec_verify_hier_rollback.restype = i32
+    lib.spec_verify_hier_rollback.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P, P, P,
+                                              P, P, i32, i32, P, P, P, i32, P, P, sz,
+                                              ctypes.POINTER(Diag), P]
     lib.kv_blocktable_truncate.restype = i32
     lib.kv_blocktable_truncate.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P]
     lib.spec_verify_device_status.restype = i32
@@ -277,6 +283,56 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
         _ptr(out["accept_len_final"]), _ptr(out["out_tokens"]), _ptr(out["num_emitted"]),
         _ptr(out["num_drop"]), _ptr(out.get("packed_tokens")), _ptr(out.get("cu_offsets")),
         _ptr(ws), ws.numel(), ctypes.byref(dg) if dg is not None else None, _stream(dev)))
+    return out
+
+
+def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
+                              block_table, seq_lens, *, block_size, max_freed, window=4,
+                              seed=0, offset=0, diag=False, workspace=None, events=None,
+                              out=None):
+    """spec_verify_hier plus the paged-KV rollback of block_table / seq_lens
+    (in place) in the same launches.  Returns the spec_verify_hier dict plus
+    freed_blocks [B, max_freed] and num_freed [B].  ``out``: a dict returned
+    by an earlier call of the same shape, whose buffers are reused.
+    Asynchronous."""
+    lib = library()
+    B, k, V = ld_logits.shape
+    dev = ld_logits.device
+    code = _dtype_code(ld_logits)
+    s0 = _logits(ld_logits, "ld_logits", B, k, ld_logits.dtype)
+    s1 = _logits(li_logits, "li_logits", B, k + 1, ld_logits.dtype)
+    s2 = _logits(lf_logits, "lf_logits", B, k + 1, ld_logits.dtype)
+    if li_logits.shape[2] != V or lf_logits.shape[2] != V:
+        raise ValueError("exit vocabularies differ")
+    _prep_common(draft_tokens, temperature, B, k, dev)
+    max_blocks = block_table.shape[1]
+    for name, t, shape in (("block_table", block_table, (B, max_blocks)),
+                           ("seq_lens", seq_lens, (B,))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_contiguous() or \
+                t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 {shape} device tensor")
+    desc = make_desc(B, k, V, code, _common_stride([s0, s1, s2], V), seed, offset)
+    need = lib.spec_verify_workspace_bytes(ctypes.byref(desc), 3)
+    if out is None:
+        ws = workspace if workspace is not None else alloc_workspace(need, dev)
+        out = dict(accept_len_inter=_int_out((B,), dev), accept_len_final=_int_out((B,), dev),
+                   out_tokens=_int_out((B, k + 1), dev), num_emitted=_int_out((B,), dev),
+                   num_drop=_int_out((B,), dev), freed_blocks=_int_out((B, max_freed), dev),
+                   num_freed=_int_out((B,), dev), workspace=ws)
+    else:
+        ws = out["workspace"]
+        if tuple(out["out_tokens"].shape) != (B, k + 1) or \
+                tuple(out["freed_blocks"].shape) != (B, max_freed):
+            raise ValueError("out buffers do not match this call's shapes")
+    dg = _make_diag(diag, events, B, k, dev, out)
+    _check(lib.spec_verify_hier_rollback(
+        ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
+        _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len_inter"]),
+        _ptr(out["accept_len_final"]), _ptr(out["out_tokens"]), _ptr(out["num_emitted"]),
+        _ptr(out["num_drop"]), int(max_blocks), int(block_size), _ptr(block_table),
+        _ptr(seq_lens), _ptr(out["freed_blocks"]) if max_freed > 0 else None, int(max_freed),
+        _ptr(out["num_freed"]), _ptr(ws), ws.numel(),
+        ctypes.byref(dg) if dg is not None else None, _stream(dev)))
     return out
 
 

@@ -28,6 +28,9 @@ struct Plan {
   int64_t ld = 0;
   size_t ws_bytes = 0;
   size_t seq_bytes = 0;   // per-sequence counters and stage-1 results
+  size_t tile_bytes = 0;  // draw tile sums of both stages
+  int nt = 0;             // draw tiles per row
+  int ns = 0;             // slices (workgroups) per sequence and stage
   int32_t exit_pos[3] = {0, 0, 0};
   int32_t exit_row0[3] = {0, 0, 0};
 };
@@ -67,8 +70,13 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   if (p->rows_total > INT32_MAX || p->rows_total * p->nc > INT32_MAX)
     return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
   p->ld = ld;
-  p->seq_bytes = (static_cast<size_t>(B) * 4 * sizeof(int32_t) + 255) / 256 * 256;
-  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes +
+  const int te = sv::tile_elems(d->dtype);
+  p->nt = (d->vocab + te - 1) / te;
+  p->ns = (p->nt + sv::kTilesPerSlice - 1) / sv::kTilesPerSlice;
+  if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
+  p->seq_bytes = (static_cast<size_t>(B) * (8 + sizeof(sv::DrawDesc)) + 255) / 256 * 256;
+  p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
+  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes +
                 static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
   return SV_OK;
 }
@@ -107,17 +115,6 @@ int32_t check_diag(const spec_verify_diag* diag) {
   return SV_OK;
 }
 
-// Sequences between a sequence's stage-1 rows and its L_f rows in the launch
-// order (tuning knob; SPEC_VERIFY_LAG overrides it).
-int lag_sequences() {
-  static const int lag = [] {
-    const char* env = std::getenv("SPEC_VERIFY_LAG");
-    const int v = env ? std::atoi(env) : sv::kLagSeqs;
-    return v < 0 ? 0 : v;
-  }();
-  return lag;
-}
-
 int32_t device_error(hipError_t e, const char* what) {
   return fail(SV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -128,12 +125,36 @@ int32_t device_error(hipError_t e, const char* what) {
     if (_s != SV_OK) return _s;   \
   } while (0)
 
+struct KvRollback {
+  int32_t max_blocks, block_size, max_freed;
+  int32_t* table;
+  int32_t* lens;
+  int32_t* freed;
+  int32_t* num_freed;
+};
+
+int32_t check_kv(int32_t batch, int32_t max_blocks, int32_t block_size, const int32_t* table,
+                 const int32_t* lens, const int32_t* drop, bool drop_required,
+                 const int32_t* freed, int32_t max_freed, const int32_t* num_freed) {
+  if (batch < 0) return fail(SV_ERR_INVALID_ARG, "batch < 0");
+  if (max_blocks < 0) return fail(SV_ERR_INVALID_ARG, "max_blocks < 0");
+  if (block_size < 1) return fail(SV_ERR_INVALID_ARG, "block_size < 1");
+  if (max_freed < 0) return fail(SV_ERR_INVALID_ARG, "max_freed < 0");
+  const bool any = batch > 0;
+  SV_TRY(check_i32(table, any && max_blocks > 0, "block_table"));
+  SV_TRY(check_i32(lens, any, "seq_lens"));
+  SV_TRY(check_i32(drop, any && drop_required, "num_drop"));
+  SV_TRY(check_i32(freed, any && max_freed > 0, "freed_blocks"));
+  SV_TRY(check_i32(num_freed, any, "num_freed"));
+  return SV_OK;
+}
+
 int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t window,
                    const void* const* logits, const int32_t* tokens, const float* temperature,
                    int32_t* accept_len, int32_t* accept_len_final, int32_t* out_tokens,
                    int32_t* num_emitted, int32_t* num_drop, int32_t* packed, int32_t* cu_offsets,
                    void* workspace, size_t workspace_bytes, const spec_verify_diag* diag,
-                   void* hip_stream) {
+                   void* hip_stream, const KvRollback* kv = nullptr) {
   Plan p;
   SV_TRY(make_plan(desc, num_exits, &p));
   if (num_exits == 3 && window < 1) return fail(SV_ERR_INVALID_ARG, "window < 1");
@@ -154,64 +175,96 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
   SV_TRY(check_diag(diag));
   SV_TRY(check_workspace(p, workspace, workspace_bytes));
+  if (kv)
+    SV_TRY(check_kv(desc->batch, kv->max_blocks, kv->block_size, kv->table, kv->lens, nullptr,
+                    false, kv->freed, kv->max_freed, kv->num_freed));
   if (!any) return SV_OK;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   char* ws = static_cast<char*>(workspace);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   int32_t* seqw = reinterpret_cast<int32_t*>(ws + sv::kFlagsBytes);
-  sv::Partial* partials = reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes);
+  float* tsum = reinterpret_cast<float*>(ws + sv::kFlagsBytes + p.seq_bytes);
+  sv::Partial* partials =
+      reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes + p.tile_bytes);
   const int B = desc->batch;
   hipError_t err;
 
-  // counters (cnt1, cnt2) and the flags start at zero
-  sv::ClearArgs ca{2 * B, seqw, flags};
-  err = sv::launch_clear(ca, st);
-  if (err != hipSuccess) return device_error(err, "clear launch");
-
-  sv::FusedArgs fa{};
-  fa.hier = num_exits == 3;
-  fa.B = B;
-  fa.k = desc->num_draft;
-  fa.V = desc->vocab;
-  fa.dtype = desc->dtype;
-  fa.nc = p.nc;
-  fa.window = num_exits == 3 ? window : 1;
-  fa.ld = p.ld;
+  sv::StatsArgs sa{};
   for (int e = 0; e < 3; ++e) {
-    fa.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
-    fa.exit_row0[e] = e < num_exits ? p.exit_row0[e] : 0;
+    sa.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+    sa.exit_pos[e] = p.exit_pos[e];
+    sa.exit_row0[e] = e < num_exits ? p.exit_row0[e] : INT32_MAX;
   }
-  fa.n1 = (2 * fa.k + 1) * p.nc;
-  fa.n2 = num_exits == 3 ? (fa.k + 1) * p.nc : 0;
-  fa.lag = num_exits == 3 ? std::min(B, lag_sequences()) : 0;
-  fa.partials = partials;
-  fa.cnt1 = seqw;
-  fa.cnt2 = seqw + B;
-  fa.st1 = reinterpret_cast<uint64_t*>(seqw + 2 * B);
-  fa.tokens = tokens;
-  fa.temperature = temperature;
-  fa.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
-  fa.key1 = static_cast<uint32_t>(desc->seed >> 32);
-  fa.offset = desc->offset;
-  fa.accept_len = accept_len;
-  fa.accept_len_final = num_exits == 3 ? accept_len_final : nullptr;
-  fa.out_tokens = out_tokens;
-  fa.num_emitted = num_emitted;
-  fa.num_drop = num_drop;
-  fa.diag_uniforms = diag ? diag->uniforms : nullptr;
-  fa.diag_probs = diag ? diag->probs : nullptr;
-  fa.diag_draws = diag ? diag->draws : nullptr;
-  fa.flags = flags;
+  sa.num_exits = num_exits;
+  sa.V = desc->vocab;
+  sa.nc = p.nc;
+  sa.dtype = desc->dtype;
+  sa.ld = p.ld;
+  sa.temperature = temperature;
+  sa.partials = partials;
+  sa.clear_words = seqw;   // the two slice counters
+  sa.n_clear = 2 * B;
+  sa.flags = flags;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
     if (err != hipSuccess) return device_error(err, "event record");
   }
-  err = sv::launch_fused(fa, p.rows_total * p.nc, st);
-  if (err != hipSuccess) return device_error(err, "verify launch");
+  err = sv::launch_stats(sa, p.rows_total, st);
+  if (err != hipSuccess) return device_error(err, "row statistics launch");
   if (diag && diag->stats_end) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
     if (err != hipSuccess) return device_error(err, "event record");
+  }
+
+  sv::VerifyArgs va{};
+  va.hier = num_exits == 3;
+  va.B = B;
+  va.k = desc->num_draft;
+  va.V = desc->vocab;
+  va.dtype = desc->dtype;
+  va.nc = p.nc;
+  va.window = num_exits == 3 ? window : 1;
+  va.nt = p.nt;
+  va.ns = p.ns;
+  va.tps = sv::kTilesPerSlice;
+  va.ld = p.ld;
+  for (int e = 0; e < 3; ++e) {
+    va.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+    va.exit_row0[e] = e < num_exits ? p.exit_row0[e] : 0;
+  }
+  va.partials = partials;
+  for (int s = 0; s < 2; ++s) {
+    va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
+    va.cnt[s] = seqw + s * B;
+  }
+  va.desc2 = reinterpret_cast<sv::DrawDesc*>(seqw + 2 * B);
+  va.tokens = tokens;
+  va.temperature = temperature;
+  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  va.offset = desc->offset;
+  va.accept_len = accept_len;
+  va.accept_len_final = num_exits == 3 ? accept_len_final : nullptr;
+  va.out_tokens = out_tokens;
+  va.num_emitted = num_emitted;
+  va.num_drop = num_drop;
+  va.diag_uniforms = diag ? diag->uniforms : nullptr;
+  va.diag_probs = diag ? diag->probs : nullptr;
+  va.diag_draws = diag ? diag->draws : nullptr;
+  va.flags = flags;
+  if (kv) {
+    va.kv_table = kv->table;
+    va.kv_lens = kv->lens;
+    va.kv_freed = kv->freed;
+    va.kv_num_freed = kv->num_freed;
+    va.kv_max_blocks = kv->max_blocks;
+    va.kv_block_size = kv->block_size;
+    va.kv_max_freed = kv->max_freed;
+  }
+  for (int stage = 0; stage < (num_exits == 3 ? 2 : 1); ++stage) {
+    err = sv::launch_slices(va, stage, st);
+    if (err != hipSuccess) return device_error(err, "verify launch");
   }
 
   if (packed) {
@@ -291,22 +344,31 @@ int32_t kv_blocktable_truncate(int32_t batch, int32_t max_blocks, int32_t block_
                                int32_t* block_table, int32_t* seq_lens,
                                const int32_t* num_drop, int32_t* freed_blocks,
                                int32_t max_freed, int32_t* num_freed, void* hip_stream) {
-  if (batch < 0) return fail(SV_ERR_INVALID_ARG, "batch < 0");
-  if (max_blocks < 0) return fail(SV_ERR_INVALID_ARG, "max_blocks < 0");
-  if (block_size < 1) return fail(SV_ERR_INVALID_ARG, "block_size < 1");
-  if (max_freed < 0) return fail(SV_ERR_INVALID_ARG, "max_freed < 0");
-  const bool any = batch > 0;
-  SV_TRY(check_i32(block_table, any && max_blocks > 0, "block_table"));
-  SV_TRY(check_i32(seq_lens, any, "seq_lens"));
-  SV_TRY(check_i32(num_drop, any, "num_drop"));
-  SV_TRY(check_i32(freed_blocks, any && max_freed > 0, "freed_blocks"));
-  SV_TRY(check_i32(num_freed, any, "num_freed"));
-  if (!any) return SV_OK;
+  SV_TRY(check_kv(batch, max_blocks, block_size, block_table, seq_lens, num_drop, true,
+                  freed_blocks, max_freed, num_freed));
+  if (batch == 0) return SV_OK;
   sv::KvArgs a{batch, max_blocks, block_size, max_freed, block_table, seq_lens,
                num_drop, freed_blocks, num_freed};
   const hipError_t err = sv::launch_kv_truncate(a, static_cast<hipStream_t>(hip_stream));
   if (err != hipSuccess) return device_error(err, "kv truncate launch");
   return SV_OK;
+}
+
+int32_t spec_verify_hier_rollback(const spec_verify_desc* desc, int32_t window,
+                                  const void* ld_logits, const void* li_logits,
+                                  const void* lf_logits, const int32_t* draft_tokens,
+                                  const float* temperature, int32_t* accept_len_inter,
+                                  int32_t* accept_len_final, int32_t* out_tokens,
+                                  int32_t* num_emitted, int32_t* num_drop, int32_t max_blocks,
+                                  int32_t block_size, int32_t* block_table, int32_t* seq_lens,
+                                  int32_t* freed_blocks, int32_t max_freed, int32_t* num_freed,
+                                  void* workspace, size_t workspace_bytes,
+                                  const spec_verify_diag* diag, void* hip_stream) {
+  const void* logits[3] = {ld_logits, li_logits, lf_logits};
+  KvRollback kv{max_blocks, block_size, max_freed, block_table, seq_lens, freed_blocks, num_freed};
+  return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
+                    accept_len_final, out_tokens, num_emitted, num_drop, nullptr, nullptr,
+                    workspace, workspace_bytes, diag, hip_stream, &kv);
 }
 
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream) {

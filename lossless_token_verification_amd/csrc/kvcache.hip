@@ -12,27 +12,9 @@ namespace {
 __global__ __launch_bounds__(kThreads) void kv_truncate_kernel(KvArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.B) return;
-  const int64_t L = a.lens[b];
-  const int64_t d = a.drop[b];
-  const int64_t bs = a.block_size;
-  const int64_t used = (L + bs - 1) / bs;
-  const int64_t keep = (L - d + bs - 1) / bs;
-  const bool ok = d >= 0 && d <= L && used <= a.max_blocks && used - keep <= a.max_freed;
-  int32_t* row = a.table + static_cast<int64_t>(b) * a.max_blocks;
-  int32_t* fr = a.freed ? a.freed + static_cast<int64_t>(b) * a.max_freed : nullptr;
-  if (!ok) {
-    for (int i = 0; i < a.max_freed; ++i) fr[i] = -1;
-    a.num_freed[b] = -1;
-    return;
-  }
-  const int n = static_cast<int>(used - keep);
-  for (int i = 0; i < n; ++i) {
-    fr[i] = row[keep + i];
-    row[keep + i] = -1;
-  }
-  for (int i = n; i < a.max_freed; ++i) fr[i] = -1;
-  a.num_freed[b] = n;
-  a.lens[b] = static_cast<int32_t>(L - d);
+  kv_rollback_one(a.table + static_cast<int64_t>(b) * a.max_blocks, a.lens + b, a.drop[b],
+                  a.freed ? a.freed + static_cast<int64_t>(b) * a.max_freed : nullptr,
+                  a.num_freed + b, a.max_blocks, a.block_size, a.max_freed);
 }
 
 }  // namespace

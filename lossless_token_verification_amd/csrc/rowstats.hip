@@ -1,0 +1,49 @@
+// The HBM stream: partial softmax statistics of every 64 KiB chunk of every
+// logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk);
+// the first workgroups also clear the slice counters of the verification
+// stages that follow on the same stream.
+#include "sv_stats.h"
+
+namespace sv {
+
+namespace {
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
+  constexpr int ES = DT == 1 ? 2 : 4;
+  constexpr int CE = kChunkBytes / ES;
+  __shared__ Red lds[kWaves];
+  const int tid = threadIdx.x;
+  {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
+    if (i < a.n_clear) a.clear_words[i] = 0;
+    if (i == 0) a.flags[0] = 0u;
+  }
+  const int row = blockIdx.x / a.nc;
+  const int chunk = blockIdx.x - row * a.nc;
+  int e = 0;
+  if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
+  if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
+  const int local = row - a.exit_row0[e];
+  const int b = local / a.exit_pos[e];
+  const float tau = a.temperature ? a.temperature[b] : 1.0f;
+  const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
+  const float s = greedy ? 0.0f : kLog2e / tau;
+  const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
+  const int e0 = chunk * CE;
+  const Partial p = chunk_stats<DT>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds);
+  if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
+}
+
+}  // namespace
+
+hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(rows_total * a.nc));
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(rowstats_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(rowstats_kernel<0>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

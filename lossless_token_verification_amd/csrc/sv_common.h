@@ -43,26 +43,52 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 16, "Partial layout");
 
-// Workspace: [flags (256 B)] [cnt1, cnt2, st1: 4 int32 per sequence, padded
-// to 256 B] [partials: rows_total * nc]
+// Workspace: [flags (256 B)] [cnt1, cnt2: 8 B per sequence] [desc2: 32 B per
+// sequence] [tile sums: 2 * B * nt floats] [partials: rows * nc], each area
+// padded to 256 B.
 constexpr size_t kFlagsBytes = 256;
-constexpr int kLagSeqs = 32;
+// Draw tiles each workgroup of a verification stage sums.
+constexpr int kTilesPerSlice = 128;
 
-// One launch of the fused kernel: the HBM stream of row statistics plus, for
-// each sequence, the verification run by the workgroup that completes its
-// statistics.
-struct FusedArgs {
+// Row statistics of every logit row (the HBM stream).
+struct StatsArgs {
+  const void* exit_ptr[3];
+  int32_t exit_pos[3];     // rows per sequence in each exit (k or k + 1)
+  int32_t exit_row0[3];    // first global row id of each exit
+  int32_t num_exits, V, nc, dtype;
+  int64_t ld;              // row stride in elements
+  const float* temperature;
+  Partial* partials;       // [rows_total * nc]
+  int32_t* clear_words;    // zeroed by the first workgroups (slice counters)
+  int32_t n_clear;
+  uint32_t* flags;
+};
+
+// What the stage-2 draw of one sequence needs, written by the workgroup that
+// took the stage-2 decision and read by the slice workgroups of the next
+// launch.
+struct DrawDesc {
+  int32_t apos;            // position of the draw; -1: no draw left
+  int32_t a1;              // stage-1 accept count
+  float v;                 // draw uniform
+  float cp, isp;           // p row: reference and 1 / S
+  float cq, isq;           // q row: reference and 1 / S
+  int32_t pad;
+};
+static_assert(sizeof(DrawDesc) == 32, "DrawDesc layout");
+
+// The verification launches (stage 1 with its draw, stage-2 draw).
+struct VerifyArgs {
   int32_t hier;            // 0: single stage (q = exit 0, p = exit 1); 1: L_d, L_i, L_f
   int32_t B, k, V, dtype, nc, window;
-  int64_t ld;              // row stride in elements
+  int32_t nt, ns, tps;     // draw tiles per row, slices per sequence, tiles per slice
+  int64_t ld;
   const void* exit_ptr[3];
-  int32_t exit_row0[3];    // first global row id of each exit (partials layout)
-  int32_t n1, n2;          // workgroups per sequence: stage-1 rows, L_f rows
-  int32_t lag;             // L_f rows of sequence b follow stage-1 rows of b + lag
-  Partial* partials;       // [rows_total * nc]
-  int32_t* cnt1;           // [B] stage-1 chunks done
-  int32_t* cnt2;           // [B] L_f chunks done + 1 when stage 1 is done
-  uint64_t* st1;           // [B] stage-1 result: a1 | (correction or bonus token) << 32
+  int32_t exit_row0[3];
+  const Partial* partials;
+  float* tsum[2];          // [B, nt] tile sums of each stage's draw
+  int32_t* cnt[2];         // [B] slices done per stage
+  DrawDesc* desc2;         // [B] stage-2 draw left for the second launch
   const int32_t* tokens;
   const float* temperature;
   uint32_t key0, key1, offset;
@@ -75,12 +101,12 @@ struct FusedArgs {
   double* diag_probs;
   double* diag_draws;
   uint32_t* flags;
-};
-
-struct ClearArgs {
-  int32_t n;
-  int32_t* words;          // n int32 set to 0
-  uint32_t* flags;
+  // optional paged-KV rollback of every sequence once its result is known
+  int32_t* kv_table;       // [B, kv_max_blocks] or NULL
+  int32_t* kv_lens;        // [B]
+  int32_t* kv_freed;       // [B, kv_max_freed] or NULL
+  int32_t* kv_num_freed;   // [B]
+  int32_t kv_max_blocks, kv_block_size, kv_max_freed;
 };
 
 struct PackArgs {
@@ -100,40 +126,54 @@ struct KvArgs {
   int32_t* num_freed;
 };
 
-hipError_t launch_clear(const ClearArgs& a, hipStream_t st);
-hipError_t launch_fused(const FusedArgs& a, int64_t items, hipStream_t st);
+hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);
+hipError_t launch_slices(const VerifyArgs& a, int stage, hipStream_t st);
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_kv_truncate(const KvArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // device helpers
 
-// Publication of per-sequence data between workgroups without cache-wide
-// fences: writers swap the words in with device-scope atomics and wait for the
-// swaps to return before counting themselves done; readers load them with
-// device-scope atomic loads, which read the coherent copy.
-__device__ __forceinline__ void publish_u64(uint64_t* p, uint64_t v) {
-  const unsigned long long old = atomicExch(reinterpret_cast<unsigned long long*>(p),
-                                            static_cast<unsigned long long>(v));
-  asm volatile("" ::"v"(old));   // the swap has completed before anything later is issued
+// Tile sums pass between the workgroups of one launch without cache-wide
+// fences: writers store them with device-scope atomic stores (written through
+// to the coherent level) and wait for the stores to complete before counting
+// themselves done; the last workgroup reads them with device-scope atomic
+// loads.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t fetch_u64(const uint64_t* p) {
+__device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void publish_partial(Partial* dst, const Partial& v) {
-  uint64_t* w = reinterpret_cast<uint64_t*>(dst);
-  publish_u64(w, static_cast<uint64_t>(__float_as_uint(v.key)) |
-                     (static_cast<uint64_t>(static_cast<uint32_t>(v.amax)) << 32));
-  publish_u64(w + 1, static_cast<uint64_t>(__double_as_longlong(v.S)));
-}
-__device__ __forceinline__ Partial fetch_partial(const Partial* src) {
-  const uint64_t* w = reinterpret_cast<const uint64_t*>(src);
-  const uint64_t a = fetch_u64(w), b = fetch_u64(w + 1);
-  Partial r;
-  r.key = __uint_as_float(static_cast<uint32_t>(a));
-  r.amax = static_cast<int32_t>(static_cast<uint32_t>(a >> 32));
-  r.S = __longlong_as_double(static_cast<long long>(b));
-  return r;
+// Waits until every memory operation this wavefront issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Rolls back the paged-KV state of one sequence: drops its last `drop` slots,
+// moves the ids of blocks left without a slot to freed[] in ascending logical
+// order (-1 padded) and clears their table entries.  A sequence whose drop is
+// outside [0, L], whose L exceeds the table, or that would free more than
+// max_freed blocks is left unchanged and gets num_freed = -1.  One thread.
+__device__ __forceinline__ void kv_rollback_one(int32_t* row, int32_t* len, int64_t drop,
+                                                int32_t* freed, int32_t* num_freed,
+                                                int max_blocks, int block_size, int max_freed) {
+  const int64_t L = *len;
+  const int64_t bs = block_size;
+  const int64_t used = (L + bs - 1) / bs;
+  const int64_t keep = (L - drop + bs - 1) / bs;
+  const bool ok = drop >= 0 && drop <= L && used <= max_blocks && used - keep <= max_freed;
+  if (!ok) {
+    for (int i = 0; i < max_freed; ++i) freed[i] = -1;
+    *num_freed = -1;
+    return;
+  }
+  const int n = static_cast<int>(used - keep);
+  for (int i = 0; i < n; ++i) {
+    freed[i] = row[keep + i];
+    row[keep + i] = -1;
+  }
+  for (int i = n; i < max_freed; ++i) freed[i] = -1;
+  *num_freed = n;
+  *len = static_cast<int32_t>(L - drop);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

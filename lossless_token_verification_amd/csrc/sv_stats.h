@@ -124,10 +124,6 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
     }
     m = fmaxf(fmaxf(m0, m1), xt);
     const bool empty = !(m > -INFINITY);   // no finite element in this thread's share
-    // Decode again below instead of keeping 8 decoded floats per vector live
-    // (that would double the registers and halve the waves per SIMD).
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) asm volatile("" : "+v"(buf[i]));
 
     if (greedy) {
       // lowest index attaining the thread's maximum

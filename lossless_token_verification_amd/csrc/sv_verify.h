@@ -1,16 +1,18 @@
-// Per-sequence verification, run by one 256-thread workgroup once the
-// statistics of the sequence's rows are complete:
+// Per-sequence verification (one verification stage, all sequences).
 //
-//   1. merge the chunk partials of the rows into (reference c, sum S) or
-//      (max, argmax) per (exit, position);
-//   2. wavefront 0, lane j = position j: gather the logits of the drafted token
-//      in the draft and target rows, p(x) and q(x), one Philox4x32-10 block for
-//      (j, b, stage, offset), accept iff u * q(x) < p(x); a ballot gives the
-//      first rejection (windows of the given size are examined in order);
-//   3. the whole workgroup draws the correction from max(0, p - q), or the bonus
-//      from p, at the stop position by an inverse CDF: tile sums of the weights
-//      (one 16-byte load per lane and tile) into LDS, a workgroup scan of the
-//      tile sums in fp64, then one wavefront rescans the selected tile.
+// A stage runs as B * ns workgroups, ns slices of the vocabulary per sequence.
+// Every workgroup of a sequence first takes the stage's decision itself (the
+// same bits in every slice):
+//   1. merge the chunk partials of the sequence's rows into (reference c,
+//      sum S) or (max, argmax) per (exit, position);
+//   2. wavefront 0, lane j = position j: gather the logits of the drafted
+//      token in the draft and target rows, p(x) and q(x), one Philox4x32-10
+//      block for (j, b, stage, offset), accept iff u * q(x) < p(x); a ballot
+//      gives the first rejection (windows of the given size examined in order).
+// Then each workgroup sums the draw weights -- max(0, p - q) for a correction,
+// p for the bonus -- over its slice of 16 tiles (one 16-byte load per lane and
+// row per tile), and the last workgroup of the sequence locates the token: an
+// fp64 scan of the tile sums, then one wavefront rescans the chosen tile.
 //
 // Stage 1 (or the single stage) compares the draft exit with the target exit;
 // stage 2 of the hierarchy compares L_i with L_f on the tentative tokens (HiSpec
@@ -22,6 +24,9 @@
 #include "sv_common.h"
 
 namespace sv {
+
+// Tiles each wavefront of a draw loads before summing them.
+constexpr int kDrawGroup = 4;
 
 struct RowStat {
   float key;    // c (sampled) or max (greedy)
@@ -36,15 +41,20 @@ struct DrawResult {
 };
 
 struct VerifyShared {
+  // draw tile sums of the one-workgroup fallback draw; also the staging area
+  // of the chunk partials when they are merged
+  alignas(16) float tiles[kMaxTiles];
   RowStat st[3][kMaxPositions];
-  float tiles[kMaxTiles];
-  double dscan[kThreads];
   int iscr[8];
   double dscr[8];
   int toks[kMaxPositions];   // tokens of the current stage
-  float vs[kMaxPositions];   // draw uniforms of the current stage
+  float vs[kMaxPositions];   // draw uniforms of the last chain decided
+  float vs1[kMaxPositions];  // stage-1 draw uniforms (hierarchy)
+  float vs2[kMaxPositions];  // stage-2 draw uniforms (hierarchy)
+  float us2[kMaxPositions];  // stage-2 accept uniforms (hierarchy)
   int sh[8];
 };
+static_assert(sizeof(float) * kMaxTiles >= 1024 * sizeof(Partial), "partial staging");
 
 template <int DT>
 struct RowT {
@@ -107,38 +117,51 @@ __device__ __forceinline__ float lane_weight_sum(const float (&xp)[RowT<DT>::VPE
   return w[0];
 }
 
-// Inverse-CDF draw over the weights of one row (pair), executed by the whole
-// workgroup.  Returns y = the smallest index with C(y) > v * R, or, when
-// rounding leaves none, the largest index with a positive weight; y = -1 when
-// R == 0.  All threads must call it (it contains barriers).
+// Sums of the draw weights over tiles [t_begin, t_end) of one row (pair),
+// written to out[t] (coherent device-scope stores when `coherent`).  Each
+// wavefront takes groups of G consecutive tiles; the loads of its next group
+// are issued before the current group is summed (two groups in flight).
 template <int DT>
-__device__ DrawResult draw_tokens(const char* prow, const RowStat& ps, const char* qrow,
-                                  const RowStat& qs, bool has_q, float s, int V, float v,
-                                  VerifyShared& sm) {
+__device__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
+                          const RowStat& qs, bool has_q, float s, int V, int t_begin, int t_end,
+                          float* out, bool coherent) {
   constexpr int VPE = RowT<DT>::VPE;
   constexpr int ES = RowT<DT>::ES;
   constexpr int TE = kWave * VPE;
+  constexpr int G = kDrawGroup;
+  constexpr int stride = kWaves * G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int NT = (V + TE - 1) / TE;
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) |
                         (has_q ? reinterpret_cast<uintptr_t>(qrow) : 0)) & 15) == 0;
   const float cp = ps.key, isp = ps.inv_S;
   const float cq = has_q ? qs.key : 0.0f, isq = has_q ? qs.inv_S : 0.0f;
-  float* tiles = sm.tiles;
 
-  // Pass 1: tile sums.  Wavefront w takes groups of G consecutive tiles, the
-  // groups of the four wavefronts interleaved; all G loads are issued first.
-  constexpr int G = 4;
-  for (int t0 = wave * G; t0 < NT; t0 += kWaves * G) {
-    float sums[G];
-    if (vec_ok && (t0 + G) * TE <= V) {
-      u32x4 vp[G], vq[G];
+  // vector loads of a whole group when it lies inside the row
+  auto fetch = [&](int t0, u32x4 (&vp)[G], u32x4 (&vq)[G]) -> bool {
+    if (!(t0 < t_end && vec_ok && (t0 + G) * TE <= V)) return false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t off = static_cast<int64_t>((t0 + g) * TE + lane * VPE) * ES;
+      vp[g] = *reinterpret_cast<const u32x4*>(prow + off);
+      if (has_q) vq[g] = *reinterpret_cast<const u32x4*>(qrow + off);
+    }
+    return true;
+  };
+  auto emit = [&](int t0, const float (&sums)[G]) {
+    if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int64_t off = static_cast<int64_t>((t0 + g) * TE + lane * VPE) * ES;
-        vp[g] = *reinterpret_cast<const u32x4*>(prow + off);
-        if (has_q) vq[g] = *reinterpret_cast<const u32x4*>(qrow + off);
+        if (t0 + g < t_end) {
+          if (coherent) store_coherent(out + t0 + g, sums[g]);
+          else out[t0 + g] = sums[g];
+        }
       }
+    }
+  };
+  // sums of a fetched group, or of a group at the row's edge (element loads)
+  auto reduce = [&](int t0, bool fetched, const u32x4 (&vp)[G], const u32x4 (&vq)[G]) {
+    float sums[G];
+    if (fetched) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float xp[VPE], xq[VPE];
@@ -162,142 +185,171 @@ __device__ DrawResult draw_tokens(const char* prow, const RowStat& ps, const cha
         sums[g] = wave_sum(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
       }
     }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        if (t0 + g < NT) tiles[t0 + g] = sums[g];
-    }
-  }
-  __syncthreads();
+    emit(t0, sums);
+  };
 
-  // Pass 2: fp64 scan of the tile sums.  Thread t owns tiles [t*per, t*per+per).
-  double* dscan = sm.dscan;
-  int* iscr = sm.iscr;
-  double* dscr = sm.dscr;
-  const int per = (NT + kThreads - 1) / kThreads;
-  const int lo = min(NT, tid * per), hi = min(NT, lo + per);
-  double mine = 0.0;
-  for (int i = lo; i < hi; ++i) mine += static_cast<double>(tiles[i]);
-  dscan[tid] = mine;
-  if (tid == 0) {
-    iscr[0] = 0x7fffffff;   // first crossing tile
-    iscr[1] = -1;           // last tile with positive sum
+  int t = t_begin + wave * G;
+  u32x4 ap[G], aq[G], bp[G], bq[G];
+  bool fa = fetch(t, ap, aq);
+  while (t < t_end) {
+    const bool fb = fetch(t + stride, bp, bq);
+    reduce(t, fa, ap, aq);
+    t += stride;
+    if (t >= t_end) break;
+    fa = fetch(t + stride, ap, aq);
+    reduce(t, fb, bp, bq);
+    t += stride;
   }
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {   // Hillis-Steele inclusive scan
-    const double add = tid >= o ? dscan[tid - o] : 0.0;
-    __syncthreads();
-    dscan[tid] += add;
-    __syncthreads();
-  }
-  const double R = dscan[kThreads - 1];
-  const double excl = tid > 0 ? dscan[tid - 1] : 0.0;
-  DrawResult res;
-  res.R = R;
-  res.t = static_cast<double>(v) * R;
-  res.y = -1;
-  res.c_lo = res.c_hi = 0.0;
-  __syncthreads();   // every thread has read the scan before any early return
-  if (!(R > 0.0)) return res;   // uniform across the workgroup
-  const double tv = res.t;
-  {
-    // The chosen token has a positive weight, so only tiles with a positive
-    // sum can hold it (this also absorbs rounding between the owners' runs).
-    double run = excl;
-    for (int i = lo; i < hi; ++i) {
-      const double nxt = run + static_cast<double>(tiles[i]);
-      if (nxt > tv && tiles[i] > 0.0f) {
-        atomicMin(&iscr[0], i);
-        break;
-      }
-      run = nxt;
-    }
-    for (int i = hi - 1; i >= lo; --i) {
-      if (tiles[i] > 0.0f) {
-        atomicMax(&iscr[1], i);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  const int T = iscr[0];
-  const bool overrun = (T == 0x7fffffff);
-  const int TT = overrun ? iscr[1] : T;   // tile to rescan
-  if (TT >= lo && TT < hi) {
-    double run = excl;
-    for (int i = lo; i < TT; ++i) run += static_cast<double>(tiles[i]);
-    dscr[0] = run;
-  }
-  __syncthreads();
+}
 
-  // Pass 3: wavefront 0 rescans tile TT element by element in fp64.
-  if (wave == 0) {
-    const int e = TT * TE + lane * VPE;
-    float xp[VPE], xq[VPE], w[VPE];
-    load_group<DT>(prow, e, V, vec_ok, xp);
-    if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
-    double lsum = 0.0;
-#pragma unroll
-    for (int q = 0; q < VPE; ++q) {
-      w[q] = weight(xp[q], has_q ? xq[q] : 0.0f, s, cp, isp, cq, isq, has_q);
-      lsum += static_cast<double>(w[q]);
-    }
-    double incl = lsum;   // inclusive prefix of lane sums
+// Inverse CDF over NT tile sums (from LDS, or coherent loads from global when
+// `coherent`): y = the smallest index with C(y) > v * R, or, when rounding
+// leaves none, the largest index with a positive weight; y = -1 when R == 0.
+// Wavefront 0 does the work (lane l owns a contiguous run of tiles: fp64 lane
+// sums, a wavefront scan, then a rescan of the chosen tile); all threads must
+// call it (it ends with a barrier and returns the result to every thread).
+template <int DT>
+__device__ DrawResult locate(const char* prow, const RowStat& ps, const char* qrow,
+                             const RowStat& qs, bool has_q, float s, int V, float v, int NT,
+                             const float* tiles, bool coherent, VerifyShared& sm) {
+  constexpr int VPE = RowT<DT>::VPE;
+  constexpr int TE = kWave * VPE;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  if (tid < kWave) {
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) |
+                          (has_q ? reinterpret_cast<uintptr_t>(qrow) : 0)) & 15) == 0;
+    const float cp = ps.key, isp = ps.inv_S;
+    const float cq = has_q ? qs.key : 0.0f, isq = has_q ? qs.inv_S : 0.0f;
+    auto tile_at = [&](int i) -> float { return coherent ? load_coherent(tiles + i) : tiles[i]; };
+    const int per = (NT + kWave - 1) / kWave;
+    const int lo = min(NT, lane * per), hi = min(NT, lo + per);
+    double mine = 0.0;
+    for (int i = lo; i < hi; ++i) mine += static_cast<double>(tile_at(i));
+    double incl = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const double up = __shfl_up(incl, o, kWave);
       if (lane >= o) incl += up;
     }
-    const double lane_excl = __shfl_up(incl, 1, kWave);
-    double run = dscr[0] + (lane > 0 ? lane_excl : 0.0);
-    int cross = -1;
+    const double R = __shfl(incl, kWave - 1, kWave);
+    const double up1 = __shfl_up(incl, 1, kWave);
+    const double excl = lane > 0 ? up1 : 0.0;
+    const double tv = static_cast<double>(v) * R;
+    int y = -1;
     double c_lo = 0.0, c_hi = 0.0;
-    int lastpos = -1;
-    double last_lo = 0.0, last_hi = 0.0;
+    if (R > 0.0) {
+      // The chosen token has a positive weight, so only tiles with a positive
+      // sum can hold it (this also absorbs rounding between the lanes' runs).
+      int cross_t = -1, last_t = -1;
+      double cross_base = 0.0, last_base = 0.0, run = excl;
+      for (int i = lo; i < hi; ++i) {
+        const float ti = tile_at(i);
+        const double nxt = run + static_cast<double>(ti);
+        if (ti > 0.0f) {
+          if (cross_t < 0 && nxt > tv) {
+            cross_t = i;
+            cross_base = run;
+          }
+          last_t = i;
+          last_base = run;
+        }
+        run = nxt;
+      }
+      const unsigned long long cmask = __ballot(cross_t >= 0);
+      const bool overrun = cmask == 0;
+      int TT;
+      double base;
+      if (!overrun) {
+        const int src = __ffsll(cmask) - 1;
+        TT = __shfl(cross_t, src, kWave);
+        base = __shfl(cross_base, src, kWave);
+      } else {
+        const unsigned long long lmask = __ballot(last_t >= 0);
+        const int src = 63 - __clzll(lmask);
+        TT = __shfl(last_t, src, kWave);
+        base = __shfl(last_base, src, kWave);
+      }
+      // rescan tile TT element by element in fp64
+      const int e = TT * TE + lane * VPE;
+      float xp[VPE], xq[VPE], w[VPE];
+      load_group<DT>(prow, e, V, vec_ok, xp);
+      if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
+      double lsum = 0.0;
 #pragma unroll
-    for (int q = 0; q < VPE; ++q) {
-      const double nxt = run + static_cast<double>(w[q]);
-      if (!overrun && cross < 0 && nxt > tv && w[q] > 0.0f) {
-        cross = q;
-        c_lo = run;
-        c_hi = nxt;
+      for (int q = 0; q < VPE; ++q) {
+        w[q] = weight(xp[q], has_q ? xq[q] : 0.0f, s, cp, isp, cq, isq, has_q);
+        lsum += static_cast<double>(w[q]);
       }
-      if (w[q] > 0.0f) {
-        lastpos = q;
-        last_lo = run;
-        last_hi = nxt;
+      double li = lsum;   // inclusive prefix of lane sums
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double up = __shfl_up(li, o, kWave);
+        if (lane >= o) li += up;
       }
-      run = nxt;
+      const double lup = __shfl_up(li, 1, kWave);
+      double r2 = base + (lane > 0 ? lup : 0.0);
+      int cross = -1, lastpos = -1;
+      double x_lo = 0.0, x_hi = 0.0, l_lo = 0.0, l_hi = 0.0;
+#pragma unroll
+      for (int q = 0; q < VPE; ++q) {
+        const double nxt = r2 + static_cast<double>(w[q]);
+        if (w[q] > 0.0f) {
+          if (!overrun && cross < 0 && nxt > tv) {
+            cross = q;
+            x_lo = r2;
+            x_hi = nxt;
+          }
+          lastpos = q;
+          l_lo = r2;
+          l_hi = nxt;
+        }
+        r2 = nxt;
+      }
+      const unsigned long long xm = __ballot(cross >= 0);
+      if (xm) {
+        const int src = __ffsll(xm) - 1;
+        y = TT * TE + src * VPE + __shfl(cross, src, kWave);
+        c_lo = __shfl(x_lo, src, kWave);
+        c_hi = __shfl(x_hi, src, kWave);
+      } else {
+        // no crossing: the last element of the tile with a positive weight
+        const unsigned long long pm = __ballot(lastpos >= 0);
+        const int src = pm ? 63 - __clzll(pm) : 0;
+        const int yq = __shfl(lastpos, src, kWave);
+        c_lo = __shfl(l_lo, src, kWave);
+        c_hi = __shfl(l_hi, src, kWave);
+        y = pm ? TT * TE + src * VPE + yq : -1;
+      }
     }
-    const unsigned long long cm = __ballot(cross >= 0);
-    if (cm) {
-      const int src = __ffsll(cm) - 1;
-      const int yq = __shfl(cross, src, kWave);
-      const double lo_ = __shfl(c_lo, src, kWave), hi_ = __shfl(c_hi, src, kWave);
-      if (lane == 0) {
-        iscr[2] = TT * TE + src * VPE + yq;
-        dscr[1] = lo_;
-        dscr[2] = hi_;
-      }
-    } else {
-      // no crossing: the last element of the tile with a positive weight
-      const unsigned long long pm = __ballot(lastpos >= 0);
-      const int src = pm ? 63 - __clzll(pm) : 0;
-      const int yq = __shfl(lastpos, src, kWave);
-      const double lo_ = __shfl(last_lo, src, kWave), hi_ = __shfl(last_hi, src, kWave);
-      if (lane == 0) {
-        iscr[2] = pm ? TT * TE + src * VPE + yq : -1;
-        dscr[1] = lo_;
-        dscr[2] = hi_;
-      }
+    if (lane == 0) {
+      sm.iscr[2] = y;
+      sm.dscr[0] = R;
+      sm.dscr[1] = tv;
+      sm.dscr[2] = c_lo;
+      sm.dscr[3] = c_hi;
     }
   }
   __syncthreads();
-  res.y = iscr[2];
-  res.c_lo = dscr[1];
-  res.c_hi = dscr[2];
+  DrawResult res;
+  res.y = sm.iscr[2];
+  res.R = sm.dscr[0];
+  res.t = sm.dscr[1];
+  res.c_lo = sm.dscr[2];
+  res.c_hi = sm.dscr[3];
   __syncthreads();   // scratch may be reused by the caller
   return res;
+}
+
+// A whole draw by one workgroup (the rare R == 0 fallback to p).
+template <int DT>
+__device__ DrawResult draw_tokens(const char* prow, const RowStat& ps, const char* qrow,
+                                  const RowStat& qs, bool has_q, float s, int V, float v,
+                                  VerifyShared& sm) {
+  constexpr int TE = kWave * RowT<DT>::VPE;
+  const int NT = (V + TE - 1) / TE;
+  tile_pass<DT>(prow, ps, qrow, qs, has_q, s, V, 0, NT, sm.tiles, false);
+  __syncthreads();
+  return locate<DT>(prow, ps, qrow, qs, has_q, s, V, v, NT, sm.tiles, false, sm);
 }
 
 __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool greedy) {
@@ -306,7 +358,7 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool gre
     r.key = -INFINITY;
     r.amax = 0x7fffffff;
     for (int c = 0; c < nc; ++c) {
-      const Partial q = fetch_partial(pp + c);
+      const Partial q = pp[c];
       if (q.key > r.key || (q.key == r.key && q.amax < r.amax)) {
         r.key = q.key;
         r.amax = q.amax;
@@ -317,10 +369,10 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool gre
   } else {
     // the reference of the whole row first, then the rescaled sums
     float cm = -INFINITY;
-    for (int c = 0; c < nc; ++c) cm = fmaxf(cm, fetch_partial(pp + c).key);
+    for (int c = 0; c < nc; ++c) cm = fmaxf(cm, pp[c].key);
     double S = 0.0;
     for (int c = 0; c < nc; ++c) {
-      const Partial q = fetch_partial(pp + c);
+      const Partial q = pp[c];
       if (q.S > 0.0) S += q.S * exp2(static_cast<double>(q.key) - static_cast<double>(cm));
     }
     r.key = cm;
@@ -331,23 +383,24 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int nc, bool gre
   return r;
 }
 
-// Per-sequence context shared by the two stages.
+// Per-sequence context of one verification stage.
 template <int DT>
 struct SeqCtx {
-  const FusedArgs& a;
+  const VerifyArgs& a;
   VerifyShared& sm;
   int b, k, V;
   bool greedy;
   float s;
 
-  __device__ SeqCtx(const FusedArgs& a_, VerifyShared& sm_, int b_) : a(a_), sm(sm_), b(b_) {
+  __device__ SeqCtx(const VerifyArgs& a_, VerifyShared& sm_, int b_, bool report)
+      : a(a_), sm(sm_), b(b_) {
     k = a.k;
     V = a.V;
     const float tau = a.temperature ? a.temperature[b] : 1.0f;
     const bool bad_tau = !(tau >= 0.0f) || !(tau < INFINITY);
     greedy = !(tau > 0.0f) || bad_tau;
     s = greedy ? 0.0f : kLog2e / tau;
-    if (bad_tau && threadIdx.x == 0) atomicOr(a.flags, kFlagTemperature);
+    if (report && bad_tau && threadIdx.x == 0) atomicOr(a.flags, kFlagTemperature);
   }
 
   __device__ int positions(int e) const { return e == 0 ? k : k + 1; }
@@ -357,19 +410,185 @@ struct SeqCtx {
            (static_cast<int64_t>(b) * positions(e) + j) * a.ld * RowT<DT>::ES;
   }
 
-  // Merged statistics of positions [0, n) of exit e into sm.st[e] (all threads).
-  __device__ void merge(int e, int n) {
-    const int tid = threadIdx.x;
-    if (tid < n) {
-      const int64_t row = a.exit_row0[e] + static_cast<int64_t>(b) * positions(e) + tid;
-      sm.st[e][tid] = merge_row(a.partials + row * a.nc, a.nc, greedy);
+  // Merged statistics of positions [0, n) of exit e into sm.st[e]; threads
+  // [t0, t0 + n) do the work.
+  __device__ void merge(int e, int n, int t0) {
+    const int t = static_cast<int>(threadIdx.x) - t0;
+    if (t >= 0 && t < n) {
+      const int64_t row = a.exit_row0[e] + static_cast<int64_t>(b) * positions(e) + t;
+      sm.st[e][t] = merge_row(a.partials + row * a.nc, a.nc, greedy);
     }
+  }
+
+  // Merged statistics of positions [0, n_e) of exits 0..2 (n_e = 0 to skip an
+  // exit): every chunk partial is loaded once, one thread per partial, into
+  // LDS, then one thread per row merges its chunks.  All threads.
+  __device__ void merge_all(int n0, int n1, int n2) {
+    const int tid = threadIdx.x;
+    const int nc = a.nc;
+    const int rows = n0 + n1 + n2;
+    if (rows * nc > 1024) {   // too many chunks to stage: merge straight from memory
+      merge(0, n0, 0);
+      merge(1, n1, kWave);
+      __syncthreads();
+      merge(2, n2, 0);
+      __syncthreads();
+      return;
+    }
+    Partial* stage = reinterpret_cast<Partial*>(sm.tiles);
+    for (int i = tid; i < rows * nc; i += kThreads) {
+      const int r = i / nc, c = i - r * nc;
+      const int e = r < n0 ? 0 : (r < n0 + n1 ? 1 : 2);
+      const int j = r - (e == 0 ? 0 : (e == 1 ? n0 : n0 + n1));
+      const int64_t row = a.exit_row0[e] + static_cast<int64_t>(b) * positions(e) + j;
+      stage[i] = a.partials[row * nc + c];
+    }
+    __syncthreads();
+    if (tid < rows) {
+      const int e = tid < n0 ? 0 : (tid < n0 + n1 ? 1 : 2);
+      const int j = tid - (e == 0 ? 0 : (e == 1 ? n0 : n0 + n1));
+      sm.st[e][j] = merge_row(stage + tid * nc, nc, greedy);
+    }
+    __syncthreads();
+  }
+
+  // Both stages' decisions over the drafted tokens at once (hierarchy): stage 1
+  // tests x_j with q = L_d, p = L_i (a1 = first rejection, else k); stage 2
+  // tests x_j, j < a1, with q = L_i, p = L_f in windows of `window`
+  // (returned a2p = first rejection before a1, else a1).  Stage 2's test of x_j
+  // is the one it would make on the tentative tokens, since t_j = x_j for
+  // j < a1.  One gather of L_d, L_i, L_f at x_j per lane.  Fills vs1, vs2, us2.
+  __device__ int2 decide_pre(int window, bool diag) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int diag_pos = k + 1;
+    if (tid < kWave) {
+      const int j = lane;
+      bool rej1 = false, rej2 = false;
+      float u1 = NAN, v1 = NAN, u2 = NAN, v2 = NAN;
+      double p1 = NAN, q1 = NAN, p2 = NAN, q2 = NAN;
+      if (j <= k) {
+        const uint4 w1 = philox4x32_10(make_uint4(j, b, 0u, a.offset), a.key0, a.key1);
+        const uint4 w2 = philox4x32_10(make_uint4(j, b, 1u, a.offset), a.key0, a.key1);
+        u1 = uniform24(w1.x);
+        v1 = uniform24(w1.y);
+        u2 = uniform24(w2.x);
+        v2 = uniform24(w2.y);
+        sm.vs1[j] = v1;
+        sm.vs2[j] = v2;
+        sm.us2[j] = u2;
+      }
+      if (j < k) {
+        const int x = sm.toks[j];
+        const bool valid = x >= 0 && x < V;
+        if (!valid && diag) atomicOr(a.flags, kFlagTokenRange);
+        if (greedy) {
+          const bool mi = valid && x == sm.st[1][j].amax;
+          const bool mf = valid && x == sm.st[2][j].amax;
+          rej1 = !mi;
+          rej2 = !mf;
+          p1 = q2 = mi ? 1.0 : 0.0;
+          q1 = valid && x == sm.st[0][j].amax ? 1.0 : 0.0;
+          p2 = mf ? 1.0 : 0.0;
+        } else if (valid) {
+          const float ld = load_elem(row_ptr(0, j), x, DT);
+          const float li = load_elem(row_ptr(1, j), x, DT);
+          const float lf = load_elem(row_ptr(2, j), x, DT);
+          q1 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(ld, s, -sm.st[0][j].key))) /
+               sm.st[0][j].S;
+          p1 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(li, s, -sm.st[1][j].key))) /
+               sm.st[1][j].S;
+          p2 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(lf, s, -sm.st[2][j].key))) /
+               sm.st[2][j].S;
+          q2 = p1;
+          rej1 = !(static_cast<double>(u1) * q1 < p1);
+          rej2 = !(static_cast<double>(u2) * q2 < p2);
+        } else {
+          rej1 = rej2 = true;
+          p1 = q1 = p2 = q2 = 0.0;
+        }
+      }
+      const unsigned long long m1 = __ballot(rej1);
+      const int a1 = m1 ? min(k, __ffsll(m1) - 1) : k;
+      const unsigned long long m2 = __ballot(rej2);
+      int a2p = a1;
+      for (int w0 = 0; w0 < a1; w0 += window) {   // windows examined in order
+        const int w1 = min(a1, w0 + window);
+        const unsigned long long wm =
+            (w1 - w0 >= 64 ? ~0ull : ((1ull << (w1 - w0)) - 1ull)) << w0;
+        if (m2 & wm) {
+          a2p = __ffsll(m2 & wm) - 1;
+          break;
+        }
+      }
+      if (diag && j < diag_pos) {
+        const int64_t base0 = (static_cast<int64_t>(b) * 2 + 0) * diag_pos + j;
+        const int64_t base1 = (static_cast<int64_t>(b) * 2 + 1) * diag_pos + j;
+        if (a.diag_probs) {
+          a.diag_probs[base0 * 2] = j < k ? p1 : NAN;
+          a.diag_probs[base0 * 2 + 1] = j < k ? q1 : NAN;
+          a.diag_probs[base1 * 2] = j < a1 ? p2 : NAN;
+          a.diag_probs[base1 * 2 + 1] = j < a1 ? q2 : NAN;
+        }
+        if (a.diag_uniforms) {
+          a.diag_uniforms[base0 * 2] = u1;
+          a.diag_uniforms[base0 * 2 + 1] = v1;
+          a.diag_uniforms[base1 * 2] = j <= a1 ? u2 : NAN;
+          a.diag_uniforms[base1 * 2 + 1] = j <= a1 ? v2 : NAN;
+        }
+      }
+      if (lane == 0) {
+        sm.sh[2] = a1;
+        sm.sh[3] = a2p;
+      }
+    }
+    __syncthreads();
+    const int2 r = make_int2(sm.sh[2], sm.sh[3]);
+    __syncthreads();
+    return r;
+  }
+
+  // Stage 2's test of the L_i token y at position a1 (every earlier position
+  // accepted): returns true when L_f accepts it.  Writes position a1's
+  // stage-2 diagnostics.  All threads.
+  __device__ bool accept_y(int a1, int y, bool diag) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+      const bool valid = y >= 0 && y < V;
+      const float u2 = sm.us2[a1];
+      bool acc;
+      double p2 = 0.0, q2 = 0.0;
+      if (greedy) {
+        acc = valid && y == sm.st[2][a1].amax;
+        p2 = acc ? 1.0 : 0.0;
+        q2 = valid && y == sm.st[1][a1].amax ? 1.0 : 0.0;
+      } else if (valid) {
+        const float li = load_elem(row_ptr(1, a1), y, DT);
+        const float lf = load_elem(row_ptr(2, a1), y, DT);
+        q2 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(li, s, -sm.st[1][a1].key))) /
+             sm.st[1][a1].S;
+        p2 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(lf, s, -sm.st[2][a1].key))) /
+             sm.st[2][a1].S;
+        acc = static_cast<double>(u2) * q2 < p2;
+      } else {
+        acc = false;
+      }
+      if (diag && a.diag_probs) {
+        double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * (k + 1) + a1) * 2;
+        d[0] = p2;
+        d[1] = q2;
+      }
+      sm.sh[4] = acc ? 1 : 0;
+    }
+    __syncthreads();
+    const bool r = sm.sh[4] != 0;
+    __syncthreads();
+    return r;
   }
 
   // One verification chain over tokens sm.toks[0..n): q rows of exit qe, p rows
   // of exit pe, Philox stage `stage`.  Returns the accept count; leaves the
   // draw uniforms in sm.vs[0..n] (position n only with a bonus).
-  __device__ int decide(int qe, int pe, int n, int stage, bool bonus, int window) {
+  __device__ int decide(int qe, int pe, int n, int stage, bool bonus, int window, bool diag) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int diag_pos = k + 1;
     if (tid < kWave) {
@@ -388,7 +607,7 @@ struct SeqCtx {
       if (j < n) {
         const int x = sm.toks[j];
         const bool valid = x >= 0 && x < V;
-        if (!valid) atomicOr(a.flags, kFlagTokenRange);
+        if (!valid && diag) atomicOr(a.flags, kFlagTokenRange);
         if (greedy) {
           reject = !(valid && x == sm.st[pe][j].amax);
           pj = valid && x == sm.st[pe][j].amax ? 1.0 : 0.0;
@@ -407,12 +626,12 @@ struct SeqCtx {
           qj = 0.0;
         }
       }
-      if (a.diag_probs && j < diag_pos) {
+      if (diag && a.diag_probs && j < diag_pos) {
         double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + stage) * diag_pos + j) * 2;
         d[0] = j < n ? pj : NAN;
         d[1] = j < n ? qj : NAN;
       }
-      if (a.diag_uniforms && j < diag_pos) {
+      if (diag && a.diag_uniforms && j < diag_pos) {
         float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + stage) * diag_pos + j) * 2;
         d[0] = u;
         d[1] = v;
@@ -437,24 +656,7 @@ struct SeqCtx {
     return r;
   }
 
-  // Correction (has_q) or bonus token at position apos, drawn with sm.vs[apos].
-  // Uniform across the workgroup.
-  __device__ int correct(int qe, int pe, int apos, bool has_q, int stage) {
-    DrawResult r;
-    int y;
-    if (greedy) {
-      y = sm.st[pe][apos].amax;
-      r.R = r.t = r.c_lo = r.c_hi = NAN;
-    } else {
-      const float v = sm.vs[apos];
-      const char* pr = row_ptr(pe, apos);
-      const char* qr = has_q ? row_ptr(qe, apos) : nullptr;
-      r = draw_tokens<DT>(pr, sm.st[pe][apos], qr, has_q ? sm.st[qe][apos] : sm.st[pe][apos],
-                          has_q, s, V, v, sm);
-      if (r.y < 0)   // no residual mass: draw from p
-        r = draw_tokens<DT>(pr, sm.st[pe][apos], nullptr, sm.st[pe][apos], false, s, V, v, sm);
-      y = r.y;
-    }
+  __device__ void write_draw_diag(int stage, const DrawResult& r) {
     if (a.diag_draws && threadIdx.x == 0) {
       double* d = a.diag_draws + (static_cast<int64_t>(b) * 2 + stage) * 4;
       d[0] = r.R;
@@ -462,7 +664,6 @@ struct SeqCtx {
       d[2] = r.c_lo;
       d[3] = r.c_hi;
     }
-    return y;
   }
 
   __device__ void write_outputs(int emitted_n, int last_tok, int a1, int a2) {
@@ -474,83 +675,173 @@ struct SeqCtx {
       a.out_tokens[static_cast<int64_t>(b) * (k + 1) + tid] = t;
     }
     if (tid == 0) {
+      const int drop = k - (emitted_n - 1);
       a.accept_len[b] = a1;
       if (a.accept_len_final) a.accept_len_final[b] = a2;
       a.num_emitted[b] = emitted_n;
-      if (a.num_drop) a.num_drop[b] = k - (emitted_n - 1);
+      if (a.num_drop) a.num_drop[b] = drop;
+      if (a.kv_lens)
+        kv_rollback_one(a.kv_table + static_cast<int64_t>(b) * a.kv_max_blocks, a.kv_lens + b,
+                        drop, a.kv_freed + static_cast<int64_t>(b) * a.kv_max_freed,
+                        a.kv_num_freed + b, a.kv_max_blocks, a.kv_block_size,
+                        a.kv_max_freed);
     }
   }
 };
 
-// Stage 1 (or the single stage): q = exit 0, p = exit 1.  For the hierarchy
-// the result (a1, y) goes to the workspace; returns true when this workgroup
-// must also run stage 2 (its L_f rows are already complete).
+__device__ __forceinline__ void nan_draw(DrawResult& r) { r.R = r.t = r.c_lo = r.c_hi = NAN; }
+
+// Loads the drafted tokens of sequence b into sm.toks[0, n) (threads 192..).
 template <int DT>
-__device__ bool verify_stage1(const FusedArgs& a, int b, VerifyShared& sm) {
-  SeqCtx<DT> cx(a, sm, b);
-  const int tid = threadIdx.x, k = a.k;
-  const int diag_pos = k + 1;
-  if (tid >= kWave && tid < kWave + k) sm.toks[tid - kWave] = a.tokens[static_cast<int64_t>(b) * k + tid - kWave];
-  if (tid >= 2 * kWave && tid < 2 * kWave + 8 && a.diag_draws)
-    a.diag_draws[static_cast<int64_t>(b) * 8 + tid - 2 * kWave] = NAN;
-  if (!a.hier && tid >= 3 * kWave && tid < 3 * kWave + diag_pos) {
-    const int j = tid - 3 * kWave;
-    if (a.diag_probs) {
-      double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
-      d[0] = d[1] = NAN;
-    }
-    if (a.diag_uniforms) {
-      float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
-      d[0] = d[1] = NAN;
-    }
-  }
-  cx.merge(0, k);
-  __syncthreads();
-  cx.merge(1, k + 1);
-  __syncthreads();
-  const int a1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1);
-  const int y = cx.correct(0, 1, a1, a1 < k, 0);
-  if (!a.hier) {
-    cx.write_outputs(a1 + 1, y, a1, -1);
-    return false;
-  }
-  __shared__ int last;
-  if (tid == 0) {
-    a.accept_len[b] = a1;
-    publish_u64(a.st1 + b, static_cast<uint64_t>(static_cast<uint32_t>(a1)) |
-                               (static_cast<uint64_t>(static_cast<uint32_t>(y)) << 32));
-    const int old = atomicAdd(&a.cnt2[b], 1);
-    last = (old == a.n2);
-  }
-  __syncthreads();
-  return last != 0;
+__device__ __forceinline__ void load_drafts(SeqCtx<DT>& cx, int n) {
+  const int t = static_cast<int>(threadIdx.x) - 3 * kWave;
+  if (t >= 0 && t < n) cx.sm.toks[t] = cx.a.tokens[static_cast<int64_t>(cx.b) * cx.k + t];
 }
 
-// Stage 2 of the hierarchy: tentative t = (x_0..x_{a1-1}, y), q = L_i, p = L_f.
+// The draw of one stage for sequence b at position apos (p rows of exit pe,
+// q rows of exit qe when has_q): this workgroup sums its slice of tiles; the
+// last slice to finish locates the token and writes the stage's draw
+// diagnostics.  Returns the token in that workgroup and -2 in the others.
+// Uniform across the workgroup.
 template <int DT>
-__device__ void verify_stage2(const FusedArgs& a, int b, VerifyShared& sm) {
-  SeqCtx<DT> cx(a, sm, b);
+__device__ int sliced_draw(SeqCtx<DT>& cx, int slice, int qe, int pe, int apos, bool has_q,
+                           int stage, float v, const RowStat& ps, const RowStat& qs) {
+  const VerifyArgs& a = cx.a;
+  VerifyShared& sm = cx.sm;
+  const char* pr = cx.row_ptr(pe, apos);
+  const char* qr = has_q ? cx.row_ptr(qe, apos) : nullptr;
+  float* tsum = a.tsum[stage] + static_cast<int64_t>(cx.b) * a.nt;
+  const int t0 = slice * a.tps;
+  tile_pass<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, t0, min(a.nt, t0 + a.tps), tsum, true);
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) sm.sh[1] = (atomicAdd(a.cnt[stage] + cx.b, 1) == a.ns - 1);
+  __syncthreads();
+  if (!sm.sh[1]) return -2;
+  DrawResult r = locate<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, v, a.nt, tsum, true, sm);
+  if (r.y < 0)   // no residual mass: draw from p
+    r = draw_tokens<DT>(pr, ps, nullptr, ps, false, cx.s, cx.V, v, sm);
+  cx.write_draw_diag(stage, r);
+  return r.y;
+}
+
+__device__ __forceinline__ DrawDesc make_desc(int apos, int a1, float v, const RowStat& p,
+                                              const RowStat& q) {
+  DrawDesc d;
+  d.apos = apos;
+  d.a1 = a1;
+  d.v = v;
+  d.cp = p.key;
+  d.isp = p.inv_S;
+  d.cq = q.key;
+  d.isq = q.inv_S;
+  d.pad = 0;
+  return d;
+}
+
+// First launch, grid B * ns.  Every workgroup of a sequence takes stage 1's
+// decision (and, for the hierarchy, stage 2's decision on the drafted tokens
+// before a1, which does not depend on the L_i token y).  Then:
+//  - if stage 2 already rejected a drafted token, y is never emitted and is
+//    not drawn: the workgroups draw stage 2's correction right away;
+//  - otherwise they draw y; the last of them tests y at position a1 against
+//    L_f and either finishes the sequence or leaves the stage-2 draw for the
+//    second launch.
+template <int DT>
+__device__ void stage1_slice(const VerifyArgs& a, int b, int slice, VerifyShared& sm) {
+  const bool first = slice == 0;
+  SeqCtx<DT> cx(a, sm, b, first);
   const int tid = threadIdx.x, k = a.k;
-  const uint64_t r1 = fetch_u64(a.st1 + b);
-  const int a1 = static_cast<int>(static_cast<uint32_t>(r1));
-  const int y = static_cast<int>(static_cast<uint32_t>(r1 >> 32));
-  const int n2 = a1 + 1;
-  if (tid < a1) sm.toks[tid] = a.tokens[static_cast<int64_t>(b) * k + tid];
-  if (tid == a1) sm.toks[tid] = y;
-  cx.merge(1, n2);
-  __syncthreads();
-  cx.merge(2, n2);
-  __syncthreads();
-  const int a2 = cx.decide(1, 2, n2, 1, false, a.window);
-  int emitted_n, last_tok;
-  if (a2 < n2) {
-    last_tok = cx.correct(1, 2, a2, true, 1);
-    emitted_n = a2 + 1;
-  } else {
-    last_tok = y;
-    emitted_n = n2;
+  const int diag_pos = k + 1;
+  load_drafts(cx, k);
+  if (first && tid >= 2 * kWave && tid < 2 * kWave + diag_pos) {
+    const int j = tid - 2 * kWave;
+    if (!a.hier) {   // the single stage has no second stage: its diagnostics are empty
+      if (a.diag_probs) {
+        double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
+        d[0] = d[1] = NAN;
+      }
+      if (a.diag_uniforms) {
+        float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
+        d[0] = d[1] = NAN;
+      }
+    }
+    if (a.hier && j == 0) {
+      DrawDesc none;
+      none.apos = -1;
+      a.desc2[b] = none;
+    }
   }
-  cx.write_outputs(emitted_n, last_tok, a1, a2);
+  if (first && a.diag_draws && tid >= 3 * kWave && tid < 3 * kWave + 8)
+    a.diag_draws[static_cast<int64_t>(b) * 8 + tid - 3 * kWave] = NAN;
+  cx.merge_all(k, k + 1, a.hier ? k + 1 : 0);
+  int a1, a2p;
+  float v1;
+  if (a.hier) {
+    const int2 r = cx.decide_pre(a.window, first);
+    a1 = r.x;
+    a2p = r.y;
+    v1 = sm.vs1[a1];
+  } else {
+    a1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1, first);
+    a2p = a1;
+    v1 = sm.vs[a1];
+  }
+  if (a.hier && a2p < a1) {
+    // stage 2 rejects drafted token a2p: emit x_0..x_{a2p-1} and its L_f correction
+    int z;
+    if (cx.greedy) {
+      if (!first) return;
+      z = sm.st[2][a2p].amax;
+    } else {
+      z = sliced_draw<DT>(cx, slice, 1, 2, a2p, true, 1, sm.vs2[a2p], sm.st[2][a2p],
+                          sm.st[1][a2p]);
+      if (z == -2) return;
+    }
+    cx.write_outputs(a2p + 1, z, a1, a2p);
+    return;
+  }
+  // stage 1's correction or bonus token y
+  int y;
+  if (cx.greedy) {
+    if (!first) return;
+    y = sm.st[1][a1].amax;
+  } else {
+    y = sliced_draw<DT>(cx, slice, 0, 1, a1, a1 < k, 0, v1, sm.st[1][a1],
+                        sm.st[0][a1 < k ? a1 : 0]);
+    if (y == -2) return;
+  }
+  if (!a.hier) {
+    cx.write_outputs(a1 + 1, y, a1, -1);
+    return;
+  }
+  // stage 2 over t = (x_0..x_{a1-1}, y): every position before a1 is accepted
+  if (tid == 0) sm.toks[a1] = y;
+  if (cx.accept_y(a1, y, true)) {
+    cx.write_outputs(a1 + 1, y, a1, a1 + 1);
+  } else if (cx.greedy) {
+    cx.write_outputs(a1 + 1, sm.st[2][a1].amax, a1, a1);
+  } else if (tid == 0) {
+    a.desc2[b] = make_desc(a1, a1, sm.vs2[a1], sm.st[2][a1], sm.st[1][a1]);
+  }
+}
+
+// Second launch (hierarchy), grid B * ns: the stage-2 draws left by the first.
+template <int DT>
+__device__ void stage2_slice(const VerifyArgs& a, int b, int slice, VerifyShared& sm) {
+  const DrawDesc d = a.desc2[b];
+  if (d.apos < 0) return;
+  SeqCtx<DT> cx(a, sm, b, false);
+  RowStat ps, qs;
+  ps.key = d.cp;
+  ps.inv_S = d.isp;
+  qs.key = d.cq;
+  qs.inv_S = d.isq;
+  const int z = sliced_draw<DT>(cx, slice, 1, 2, d.apos, true, 1, d.v, ps, qs);
+  if (z == -2) return;
+  load_drafts(cx, d.apos);
+  __syncthreads();
+  cx.write_outputs(d.apos + 1, z, d.a1, d.apos);
 }
 
 }  // namespace sv

@@ -223,6 +223,25 @@ def test_empty_batch_is_a_no_op(sv):
     assert out["accept_len"].numel() == 0
 
 
+@pytest.mark.parametrize("dt,temps", [("bf16", (1.0,)), ("f32", (0.0, 0.8))])
+def test_hier_rollback_equals_verify_then_truncate(sv, dt, temps):
+    """The fused call gives the same verification outputs and the same KV
+    state as spec_verify_hier followed by kv_blocktable_truncate."""
+    w = workloads.make_hier(64, 8, 30011, dtype=dt, temps=temps, seed=(101, 0), ctx=(20, 200))
+    g = P.to_device(w, DEV)
+    out = _run_hier(sv, w, 3, 4, 4)
+    t1, l1 = g["block_table"].clone(), g["seq_lens"].clone()
+    f1, n1 = sv.kv_blocktable_truncate(t1, l1, out["num_drop"], 16, 1)
+    t2, l2 = g["block_table"].clone(), g["seq_lens"].clone()
+    out2 = sv.spec_verify_hier_rollback(g["ld_logits"], g["li_logits"], g["lf_logits"],
+                                        g["draft_tokens"], g["temperature"], t2, l2,
+                                        block_size=16, max_freed=1, window=4, seed=3, offset=4)
+    for key in HIER_KEYS:
+        assert torch.equal(out[key], out2[key]), key
+    assert torch.equal(t1, t2) and torch.equal(l1, l2)
+    assert torch.equal(f1, out2["freed_blocks"]) and torch.equal(n1, out2["num_freed"])
+
+
 @pytest.mark.parametrize("bs", [1, 16])
 def test_kv_blocktable_parity(sv, bs):
     rng = np.random.default_rng(bs)
