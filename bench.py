@@ -110,8 +110,8 @@ def _traffic(launch_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

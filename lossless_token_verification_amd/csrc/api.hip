@@ -73,8 +73,8 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   const int te = sv::tile_elems(d->dtype);
   p->nt = (d->vocab + te - 1) / te;
   p->ns = (p->nt + sv::kTilesPerSlice - 1) / sv::kTilesPerSlice;
-  if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
-  p->seq_bytes = (static_cast<size_t>(B) * (8 + sizeof(sv::DrawDesc)) + 255) / 256 * 256;
+  if (B * 2 * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
+  p->seq_bytes = (static_cast<size_t>(B) * 5 * sizeof(int32_t) + 255) / 256 * 256;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
   p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes +
                 static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
@@ -203,8 +203,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.ld = p.ld;
   sa.temperature = temperature;
   sa.partials = partials;
-  sa.clear_words = seqw;   // the two slice counters
-  sa.n_clear = 2 * B;
+  sa.clear_words = seqw;   // slice counters and completed-draw counters
+  sa.n_clear = 3 * B;
   sa.flags = flags;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
@@ -238,7 +238,9 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
     va.cnt[s] = seqw + s * B;
   }
-  va.desc2 = reinterpret_cast<sv::DrawDesc*>(seqw + 2 * B);
+  va.done = seqw + 2 * B;
+  va.ytok = seqw + 3 * B;
+  va.ztok = seqw + 4 * B;
   va.tokens = tokens;
   va.temperature = temperature;
   va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
@@ -262,10 +264,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     va.kv_block_size = kv->block_size;
     va.kv_max_freed = kv->max_freed;
   }
-  for (int stage = 0; stage < (num_exits == 3 ? 2 : 1); ++stage) {
-    err = sv::launch_slices(va, stage, st);
-    if (err != hipSuccess) return device_error(err, "verify launch");
-  }
+  err = sv::launch_verify(va, st);
+  if (err != hipSuccess) return device_error(err, "verify launch");
 
   if (packed) {
     sv::PackArgs pa{desc->batch, desc->num_draft, out_tokens, num_emitted, packed, cu_offsets};

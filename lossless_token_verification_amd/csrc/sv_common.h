@@ -43,9 +43,9 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 16, "Partial layout");
 
-// Workspace: [flags (256 B)] [cnt1, cnt2: 8 B per sequence] [desc2: 32 B per
-// sequence] [tile sums: 2 * B * nt floats] [partials: rows * nc], each area
-// padded to 256 B.
+// Workspace: [flags (256 B)] [cnt1, cnt2, done, ytok, ztok: 20 B per sequence]
+// [tile sums: 2 * B * nt floats] [partials: rows * nc], each area padded to
+// 256 B.
 constexpr size_t kFlagsBytes = 256;
 // Draw tiles each workgroup of a verification stage sums.
 constexpr int kTilesPerSlice = 128;
@@ -64,19 +64,6 @@ struct StatsArgs {
   uint32_t* flags;
 };
 
-// What the stage-2 draw of one sequence needs, written by the workgroup that
-// took the stage-2 decision and read by the slice workgroups of the next
-// launch.
-struct DrawDesc {
-  int32_t apos;            // position of the draw; -1: no draw left
-  int32_t a1;              // stage-1 accept count
-  float v;                 // draw uniform
-  float cp, isp;           // p row: reference and 1 / S
-  float cq, isq;           // q row: reference and 1 / S
-  int32_t pad;
-};
-static_assert(sizeof(DrawDesc) == 32, "DrawDesc layout");
-
 // The verification launches (stage 1 with its draw, stage-2 draw).
 struct VerifyArgs {
   int32_t hier;            // 0: single stage (q = exit 0, p = exit 1); 1: L_d, L_i, L_f
@@ -88,7 +75,9 @@ struct VerifyArgs {
   const Partial* partials;
   float* tsum[2];          // [B, nt] tile sums of each stage's draw
   int32_t* cnt[2];         // [B] slices done per stage
-  DrawDesc* desc2;         // [B] stage-2 draw left for the second launch
+  int32_t* done;           // [B] draws of the sequence completed
+  int32_t* ytok;           // [B] stage-1 token y
+  int32_t* ztok;           // [B] stage-2 correction drawn beside y
   const int32_t* tokens;
   const float* temperature;
   uint32_t key0, key1, offset;
@@ -127,7 +116,7 @@ struct KvArgs {
 };
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);
-hipError_t launch_slices(const VerifyArgs& a, int stage, hipStream_t st);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_kv_truncate(const KvArgs& a, hipStream_t st);
 
@@ -143,6 +132,12 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Waits until every memory operation this wavefront issued has completed.

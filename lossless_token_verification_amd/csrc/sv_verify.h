@@ -122,7 +122,7 @@ __device__ __forceinline__ float lane_weight_sum(const float (&xp)[RowT<DT>::VPE
 // wavefront takes groups of G consecutive tiles; the loads of its next group
 // are issued before the current group is summed (two groups in flight).
 template <int DT>
-__device__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
+__device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
                           const RowStat& qs, bool has_q, float s, int V, int t_begin, int t_end,
                           float* out, bool coherent) {
   constexpr int VPE = RowT<DT>::VPE;
@@ -209,7 +209,7 @@ __device__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
 // sums, a wavefront scan, then a rescan of the chosen tile); all threads must
 // call it (it ends with a barrier and returns the result to every thread).
 template <int DT>
-__device__ DrawResult locate(const char* prow, const RowStat& ps, const char* qrow,
+__device__ __forceinline__ DrawResult locate(const char* prow, const RowStat& ps, const char* qrow,
                              const RowStat& qs, bool has_q, float s, int V, float v, int NT,
                              const float* tiles, bool coherent, VerifyShared& sm) {
   constexpr int VPE = RowT<DT>::VPE;
@@ -342,7 +342,7 @@ __device__ DrawResult locate(const char* prow, const RowStat& ps, const char* qr
 
 // A whole draw by one workgroup (the rare R == 0 fallback to p).
 template <int DT>
-__device__ DrawResult draw_tokens(const char* prow, const RowStat& ps, const char* qrow,
+__device__ __attribute__((noinline)) DrawResult draw_tokens(const char* prow, const RowStat& ps, const char* qrow,
                                   const RowStat& qs, bool has_q, float s, int V, float v,
                                   VerifyShared& sm) {
   constexpr int TE = kWave * RowT<DT>::VPE;
@@ -526,8 +526,12 @@ struct SeqCtx {
         if (a.diag_probs) {
           a.diag_probs[base0 * 2] = j < k ? p1 : NAN;
           a.diag_probs[base0 * 2 + 1] = j < k ? q1 : NAN;
-          a.diag_probs[base1 * 2] = j < a1 ? p2 : NAN;
-          a.diag_probs[base1 * 2 + 1] = j < a1 ? q2 : NAN;
+          // position a1 of stage 2 belongs to the test of y when it happens
+          // (one writer per entry: stores from different XCDs are not ordered)
+          if (j != a1 || a2p < a1) {
+            a.diag_probs[base1 * 2] = j < a1 ? p2 : NAN;
+            a.diag_probs[base1 * 2 + 1] = j < a1 ? q2 : NAN;
+          }
         }
         if (a.diag_uniforms) {
           a.diag_uniforms[base0 * 2] = u1;
@@ -698,82 +702,83 @@ __device__ __forceinline__ void load_drafts(SeqCtx<DT>& cx, int n) {
   if (t >= 0 && t < n) cx.sm.toks[t] = cx.a.tokens[static_cast<int64_t>(cx.b) * cx.k + t];
 }
 
-// The draw of one stage for sequence b at position apos (p rows of exit pe,
-// q rows of exit qe when has_q): this workgroup sums its slice of tiles; the
-// last slice to finish locates the token and writes the stage's draw
-// diagnostics.  Returns the token in that workgroup and -2 in the others.
-// Uniform across the workgroup.
+// Sums slice g of a draw's tiles (p rows at pr, q rows at qr when has_q) and
+// counts it done; true in the workgroup that completes the draw.
 template <int DT>
-__device__ int sliced_draw(SeqCtx<DT>& cx, int slice, int qe, int pe, int apos, bool has_q,
-                           int stage, float v, const RowStat& ps, const RowStat& qs) {
+__device__ bool draw_slice(SeqCtx<DT>& cx, int g, int stage, const char* pr, const char* qr,
+                           bool has_q, const RowStat& ps, const RowStat& qs) {
   const VerifyArgs& a = cx.a;
   VerifyShared& sm = cx.sm;
-  const char* pr = cx.row_ptr(pe, apos);
-  const char* qr = has_q ? cx.row_ptr(qe, apos) : nullptr;
   float* tsum = a.tsum[stage] + static_cast<int64_t>(cx.b) * a.nt;
-  const int t0 = slice * a.tps;
+  const int t0 = g * a.tps;
   tile_pass<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, t0, min(a.nt, t0 + a.tps), tsum, true);
   wait_memory();
   __syncthreads();
   if (threadIdx.x == 0) sm.sh[1] = (atomicAdd(a.cnt[stage] + cx.b, 1) == a.ns - 1);
   __syncthreads();
-  if (!sm.sh[1]) return -2;
-  DrawResult r = locate<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, v, a.nt, tsum, true, sm);
+  const bool last = sm.sh[1] != 0;
+  __syncthreads();
+  return last;
+}
+
+// In the workgroup that completed a draw: locate the token from the tile sums
+// (or, with no residual mass, draw from p) and write the stage's diagnostics.
+template <int DT>
+__device__ int draw_finish(SeqCtx<DT>& cx, int stage, const char* pr, const char* qr,
+                           bool has_q, const RowStat& ps, const RowStat& qs, float v) {
+  const float* tsum = cx.a.tsum[stage] + static_cast<int64_t>(cx.b) * cx.a.nt;
+  DrawResult r = locate<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, v, cx.a.nt, tsum, true, cx.sm);
   if (r.y < 0)   // no residual mass: draw from p
-    r = draw_tokens<DT>(pr, ps, nullptr, ps, false, cx.s, cx.V, v, sm);
+    r = draw_tokens<DT>(pr, ps, nullptr, ps, false, cx.s, cx.V, v, cx.sm);
   cx.write_draw_diag(stage, r);
   return r.y;
 }
 
-__device__ __forceinline__ DrawDesc make_desc(int apos, int a1, float v, const RowStat& p,
-                                              const RowStat& q) {
-  DrawDesc d;
-  d.apos = apos;
-  d.a1 = a1;
-  d.v = v;
-  d.cp = p.key;
-  d.isp = p.inv_S;
-  d.cq = q.key;
-  d.isq = q.inv_S;
-  d.pad = 0;
-  return d;
+// The draw of one stage for sequence b at position apos (p rows of exit pe,
+// q rows of exit qe when has_q), slice `slice` of it in this workgroup.
+// Returns the token in the workgroup that completes the draw and -2 in the
+// others.  Uniform across the workgroup.
+template <int DT>
+__device__ int sliced_draw(SeqCtx<DT>& cx, int slice, int qe, int pe, int apos, bool has_q,
+                           int stage, float v, const RowStat& ps, const RowStat& qs) {
+  const char* pr = cx.row_ptr(pe, apos);
+  const char* qr = has_q ? cx.row_ptr(qe, apos) : nullptr;
+  if (!draw_slice<DT>(cx, slice, stage, pr, qr, has_q, ps, qs)) return -2;
+  return draw_finish<DT>(cx, stage, pr, qr, has_q, ps, qs, v);
 }
 
-// First launch, grid B * ns.  Every workgroup of a sequence takes stage 1's
-// decision (and, for the hierarchy, stage 2's decision on the drafted tokens
-// before a1, which does not depend on the L_i token y).  Then:
-//  - if stage 2 already rejected a drafted token, y is never emitted and is
-//    not drawn: the workgroups draw stage 2's correction right away;
-//  - otherwise they draw y; the last of them tests y at position a1 against
-//    L_f and either finishes the sequence or leaves the stage-2 draw for the
-//    second launch.
+// One launch, grid B * ns (single stage) or B * 2ns (hierarchy): workgroup w
+// of sequence b works on draw w / ns, slice w % ns.  Every workgroup takes
+// stage 1's decision itself (and, for the hierarchy, stage 2's decision on the
+// drafted tokens before a1, which does not depend on the L_i token y).  Then
+// the draws the sequence needs run side by side:
+//  - stage 2 rejected drafted token a2p < a1: y is never emitted; draw 0 is
+//    stage 2's correction at a2p, and the sequence is done;
+//  - otherwise draw 0 is y (stage 1's correction, or its bonus), and for the
+//    hierarchy draw 1 is stage 2's correction at a1 -- which depends only on
+//    the rows L_f[a1], L_i[a1] and its own uniform, not on y.  The workgroup
+//    completing the second of the two tests y against L_f: emitting t when
+//    L_f accepts it, else t[:a1] and the correction.
 template <int DT>
-__device__ void stage1_slice(const VerifyArgs& a, int b, int slice, VerifyShared& sm) {
-  const bool first = slice == 0;
+__device__ void verify_slice(const VerifyArgs& a, int b, int w, VerifyShared& sm) {
+  const int draw = w / a.ns, slice = w - draw * a.ns;
+  const bool first = w == 0;
   SeqCtx<DT> cx(a, sm, b, first);
   const int tid = threadIdx.x, k = a.k;
   const int diag_pos = k + 1;
   load_drafts(cx, k);
-  if (first && tid >= 2 * kWave && tid < 2 * kWave + diag_pos) {
+  if (first && !a.hier && tid >= 2 * kWave && tid < 2 * kWave + diag_pos) {
+    // the single stage has no second stage: its diagnostics are empty
     const int j = tid - 2 * kWave;
-    if (!a.hier) {   // the single stage has no second stage: its diagnostics are empty
-      if (a.diag_probs) {
-        double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
-        d[0] = d[1] = NAN;
-      }
-      if (a.diag_uniforms) {
-        float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
-        d[0] = d[1] = NAN;
-      }
+    if (a.diag_probs) {
+      double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
+      d[0] = d[1] = NAN;
     }
-    if (a.hier && j == 0) {
-      DrawDesc none;
-      none.apos = -1;
-      a.desc2[b] = none;
+    if (a.diag_uniforms) {
+      float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
+      d[0] = d[1] = NAN;
     }
   }
-  if (first && a.diag_draws && tid >= 3 * kWave && tid < 3 * kWave + 8)
-    a.diag_draws[static_cast<int64_t>(b) * 8 + tid - 3 * kWave] = NAN;
   cx.merge_all(k, k + 1, a.hier ? k + 1 : 0);
   int a1, a2p;
   float v1;
@@ -787,61 +792,85 @@ __device__ void stage1_slice(const VerifyArgs& a, int b, int slice, VerifyShared
     a2p = a1;
     v1 = sm.vs[a1];
   }
-  if (a.hier && a2p < a1) {
-    // stage 2 rejects drafted token a2p: emit x_0..x_{a2p-1} and its L_f correction
-    int z;
-    if (cx.greedy) {
-      if (!first) return;
-      z = sm.st[2][a2p].amax;
-    } else {
-      z = sliced_draw<DT>(cx, slice, 1, 2, a2p, true, 1, sm.vs2[a2p], sm.st[2][a2p],
-                          sm.st[1][a2p]);
-      if (z == -2) return;
+  if (first && a.diag_draws && tid < 8) {
+    // draw diagnostics of the draws that do not happen (the others are written
+    // by the workgroup completing each draw)
+    const int stage = tid / 4;
+    const bool drawn = !cx.greedy && (stage == 0 ? !(a.hier && a2p < a1) : a.hier);
+    if (!drawn) a.diag_draws[static_cast<int64_t>(b) * 8 + tid] = NAN;
+  }
+
+  if (cx.greedy) {   // argmax tokens: no draw, the first workgroup finishes
+    if (!first) return;
+    if (a.hier && a2p < a1) {
+      cx.write_outputs(a2p + 1, sm.st[2][a2p].amax, a1, a2p);
+      return;
     }
-    cx.write_outputs(a2p + 1, z, a1, a2p);
+    const int y = sm.st[1][a1].amax;
+    if (!a.hier) {
+      cx.write_outputs(a1 + 1, y, a1, -1);
+      return;
+    }
+    if (tid == 0) sm.toks[a1] = y;
+    if (cx.accept_y(a1, y, true)) cx.write_outputs(a1 + 1, y, a1, a1 + 1);
+    else cx.write_outputs(a1 + 1, sm.st[2][a1].amax, a1, a1);
     return;
   }
-  // stage 1's correction or bonus token y
-  int y;
-  if (cx.greedy) {
-    if (!first) return;
-    y = sm.st[1][a1].amax;
-  } else {
-    y = sliced_draw<DT>(cx, slice, 0, 1, a1, a1 < k, 0, v1, sm.st[1][a1],
-                        sm.st[0][a1 < k ? a1 : 0]);
-    if (y == -2) return;
+
+  // which draw this workgroup works on (one call site keeps one copy of it)
+  const bool early = a.hier && a2p < a1;   // stage 2 rejects drafted token a2p
+  if (early && draw != 0) return;
+  int stage, apos;
+  bool has_q;
+  float v;
+  if (early) {            // stage 2's correction at a2p; y is never emitted
+    stage = 1;
+    apos = a2p;
+    has_q = true;
+    v = sm.vs2[a2p];
+  } else if (draw == 0) { // y: stage 1's correction or bonus
+    stage = 0;
+    apos = a1;
+    has_q = a1 < k;
+    v = v1;
+  } else {                // stage 2's correction at a1, used if L_f rejects y
+    stage = 1;
+    apos = a1;
+    has_q = true;
+    v = sm.vs2[a1];
+  }
+  const int tok = sliced_draw<DT>(cx, slice, stage, stage + 1, apos, has_q, stage, v,
+                                  sm.st[stage + 1][apos], sm.st[stage][has_q ? apos : 0]);
+  if (tok == -2) return;
+  if (early) {
+    cx.write_outputs(a2p + 1, tok, a1, a2p);
+    return;
   }
   if (!a.hier) {
-    cx.write_outputs(a1 + 1, y, a1, -1);
+    cx.write_outputs(a1 + 1, tok, a1, -1);
     return;
   }
-  // stage 2 over t = (x_0..x_{a1-1}, y): every position before a1 is accepted
+  // this workgroup completed one of the two draws: the one completing the
+  // second finishes the sequence
+  if (tid == 0) {
+    store_coherent(draw == 0 ? a.ytok + b : a.ztok + b, tok);
+    wait_memory();
+    sm.sh[7] = atomicAdd(a.done + b, 1);
+  }
+  __syncthreads();
+  if (sm.sh[7] != 1) return;
+  if (tid == 0) {
+    sm.sh[5] = load_coherent(a.ytok + b);
+    sm.sh[6] = load_coherent(a.ztok + b);
+  }
+  __syncthreads();
+  const int y = sm.sh[5], z = sm.sh[6];
   if (tid == 0) sm.toks[a1] = y;
   if (cx.accept_y(a1, y, true)) {
     cx.write_outputs(a1 + 1, y, a1, a1 + 1);
-  } else if (cx.greedy) {
-    cx.write_outputs(a1 + 1, sm.st[2][a1].amax, a1, a1);
-  } else if (tid == 0) {
-    a.desc2[b] = make_desc(a1, a1, sm.vs2[a1], sm.st[2][a1], sm.st[1][a1]);
+  } else {
+    cx.write_outputs(a1 + 1, z, a1, a1);
   }
-}
-
-// Second launch (hierarchy), grid B * ns: the stage-2 draws left by the first.
-template <int DT>
-__device__ void stage2_slice(const VerifyArgs& a, int b, int slice, VerifyShared& sm) {
-  const DrawDesc d = a.desc2[b];
-  if (d.apos < 0) return;
-  SeqCtx<DT> cx(a, sm, b, false);
-  RowStat ps, qs;
-  ps.key = d.cp;
-  ps.inv_S = d.isp;
-  qs.key = d.cq;
-  qs.inv_S = d.isq;
-  const int z = sliced_draw<DT>(cx, slice, 1, 2, d.apos, true, 1, d.v, ps, qs);
-  if (z == -2) return;
-  load_drafts(cx, d.apos);
-  __syncthreads();
-  cx.write_outputs(d.apos + 1, z, d.a1, d.apos);
 }
 
 }  // namespace sv

@@ -1,5 +1,5 @@
-// Verification launches (see sv_verify.h): B * ns workgroups for stage 1 and
-// its draw, then (hierarchy) B * ns for the stage-2 draws left over; plus the
+// The verification launch (see sv_verify.h): B * ns workgroups take both
+// stages' decisions and draw the correction / bonus tokens; plus the
 // packed-output scan.
 #include "sv_verify.h"
 
@@ -7,15 +7,13 @@ namespace sv {
 
 namespace {
 
-template <int DT, int STAGE>
-__global__ __launch_bounds__(kThreads) void slice_kernel(VerifyArgs a) {
+template <int DT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void verify_kernel(VerifyArgs a) {
   __shared__ VerifyShared sm;
-  const int b = blockIdx.x / a.ns;
-  const int slice = blockIdx.x - b * a.ns;
-  if (STAGE == 0)
-    stage1_slice<DT>(a, b, slice, sm);
-  else
-    stage2_slice<DT>(a, b, slice, sm);
+  const int per_seq = a.hier ? 2 * a.ns : a.ns;
+  const int b = blockIdx.x / per_seq;
+  verify_slice<DT>(a, b, blockIdx.x - b * per_seq, sm);
 }
 
 // Packed (unpadded) tokens: cu_offsets by a single-workgroup scan of the
@@ -52,15 +50,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
 
 }  // namespace
 
-hipError_t launch_slices(const VerifyArgs& a, int stage, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.ns));
-  if (a.dtype == 1) {
-    if (stage == 0) hipLaunchKernelGGL((slice_kernel<1, 0>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((slice_kernel<1, 1>), grid, dim3(kThreads), 0, st, a);
-  } else {
-    if (stage == 0) hipLaunchKernelGGL((slice_kernel<0, 0>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((slice_kernel<0, 1>), grid, dim3(kThreads), 0, st, a);
-  }
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.hier ? 2 * a.ns : a.ns));
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(verify_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(verify_kernel<0>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ def test_version_and_status_strings(sv):
 
 
 def test_workspace_size_formula(sv):
-    # 256 B of flags + 40 B per sequence + 2 draw-tile sums per (sequence, tile)
+    # 256 B of flags + 20 B per sequence + 2 draw-tile sums per (sequence, tile)
     # (each area padded to 256 B) + one 16-byte partial per (row, 64 KiB chunk)
     def pad(n):
         return (n + 255) // 256 * 256
@@ -56,11 +56,11 @@ def test_workspace_size_formula(sv):
     def tiles(V, per):
         return -(-V // per)
     assert sv.workspace_bytes(256, 8, 128256, 1, 3) == \
-        256 + pad(256 * 40) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
+        256 + pad(256 * 20) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
     assert sv.workspace_bytes(64, 4, 32000, 1, 2) == \
-        256 + pad(64 * 40) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
+        256 + pad(64 * 20) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
     assert sv.workspace_bytes(32, 5, 151936, 0, 2) == \
-        256 + pad(32 * 40) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
+        256 + pad(32 * 20) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 
