@@ -11,10 +11,11 @@ Prints one JSON line: verified draft tokens/s (B*k per step), whole-step and
 row-statistics-kernel HBM bandwidth against the 8 TB/s peak, and the CPU oracle
 timed on a bounded sample of the same workload on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 300]
 """
 
 import argparse
+import csv
 import ctypes
 import hashlib
 import json
@@ -29,7 +30,17 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft tokens/s + achieved HBM GB/s (% peak), B=256 k=8 V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rowstats_hier_B256_k8_V128256_bf16_traffic.json")
-ROWSTATS_SRC = os.path.join(ROOT, "lossless_token_verification_amd", "csrc", "rowstats.hip")
+ROWSTATS_SRC = [os.path.join(ROOT, "lossless_token_verification_amd", "csrc", f)
+                for f in ("rowstats.hip", "sv_stats.h", "sv_common.h")]
+
+
+def _rowstats_sha():
+    """Digest of the sources the row-statistics kernel is compiled from."""
+    h = hashlib.sha256()
+    for fn in ROWSTATS_SRC:
+        with open(fn, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 # --- CPU baseline (the oracle, on a bounded sample of the same workload) ----
 
@@ -44,9 +55,10 @@ def _cpu_worker(seqs):
     return len(seqs)
 
 
-def cpu_baseline(sample_seqs, procs):
-    """Oracle wall time on ``sample_seqs`` sequences shaped like the workload,
-    over ``procs`` forked worker processes (started before any GPU use)."""
+def cpu_baseline(sample_seqs, procs, min_seconds):
+    """Oracle wall time over ``procs`` forked worker processes (started before
+    any GPU use) on ``sample_seqs`` sequences shaped like the workload, passed
+    through the oracle again and again until ``min_seconds`` have gone by."""
     import numpy as np
     import workloads
     w = workloads.make_hier(sample_seqs, 8, 128256, seed=(3, 1000), ctx=(512, 4096))
@@ -54,19 +66,108 @@ def cpu_baseline(sample_seqs, procs):
                 lf=workloads.to_numpy_raw(w["lf_logits"]), tok=w["draft_tokens"].numpy(),
                 temp=w["temperature"].numpy())
     del w
-    chunks = [list(c) for c in np.array_split(np.arange(sample_seqs), procs * 2) if len(c)]
+    chunks = [list(c) for c in np.array_split(np.arange(sample_seqs), procs) if len(c)]
     ctx = mp.get_context("fork")
     with ctx.Pool(procs) as pool:
         pool.map(_cpu_worker, [[0]] * procs)          # warm the workers
+        done, passes = 0, 0
         t0 = time.perf_counter()
-        done = sum(pool.map(_cpu_worker, chunks))
-        dt = time.perf_counter() - t0
+        while True:
+            done += sum(pool.map(_cpu_worker, chunks))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
     _CPU.clear()
     return dict(value=done * 8 / dt, unit="verified draft tokens/s", cores=procs, kind="oracle",
-                sample=f"{done} sequences of the B=256 k=8 V=128256 bf16 hierarchical workload "
-                       f"(L_d, L_i, L_f logits, window 4), NumPy float64 oracle over {procs} "
-                       f"processes, {dt:.2f} s wall",
+                sample=f"{passes} passes over {sample_seqs} sequences ({done} sequence "
+                       f"verifications) of the B=256 k=8 V=128256 bf16 hierarchical workload "
+                       f"(L_d, L_i, L_f logits, window 4), NumPy float64 oracle, one worker "
+                       f"process per core, {dt:.1f} s wall",
                 seconds=dt)
+
+
+# --- HBM traffic from rocprofv3 counters -------------------------------------
+
+COPY_ELEMS = 1 << 28            # fp32 elements of the calibration copy (1 GiB each way)
+
+
+def calibration_copy(dev):
+    """A plain copy of known size (reads and writes COPY_ELEMS * 4 bytes),
+    launched next to the profiled steps so that FETCH_SIZE / WRITE_SIZE can
+    be converted into bytes."""
+    import torch
+    x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 2.0, out=y)
+    torch.cuda.synchronize()
+    del x, y
+
+
+def _counter_rows(d):
+    """(dispatch id, kernel name, counter name, value) of every dispatch in the
+    counter_collection.csv files under directory ``d``."""
+    out = []
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn), newline="") as f:
+                for r in csv.DictReader(f):
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                                float(r["Counter_Value"])))
+    return out
+
+
+def _per_dispatch(rows, counter, ids):
+    vals = [v for i, _, c, v in rows if c == counter and i in ids]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for the requested kernel")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _ids(rows):
+    """Dispatch ids of the row-statistics kernel, and of the calibration copy
+    (the last three dispatches of the process)."""
+    names = {i: n for i, n, _, _ in rows}
+    stats = {i for i, n in names.items() if "rowstats_kernel<1>" in n}
+    last = sorted(names)[-3:]
+    if len({names[i] for i in last}) != 1 or any(i in stats for i in last):
+        raise SystemExit("the last three dispatches are not the calibration copy")
+    return stats, set(last)
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Write the traffic summary of the row-statistics kernel from two
+    counter runs (FETCH_SIZE, then WRITE_SIZE), each scaled by the reading of
+    the same counter for the calibration copy."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    (fs, fc), (ws, wc) = _ids(fr), _ids(wr)
+    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", fs)
+    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", ws)
+    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", fc)
+    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", wc)
+    copy_bytes = COPY_ELEMS * 4
+    kf, kw = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
+    fetch_b, write_b = f_k * 1024.0 * kf, w_k * 1024.0 * kw
+    sha = _rowstats_sha()
+    out = {
+        "kernel": "rowstats_kernel<bf16>",
+        "workload": "hierarchical verify, B=256 k=8 V=128256 bf16",
+        "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
+        "dispatches": [nf, nw],
+        "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1),
+        "copy_bytes_each_way": copy_bytes,
+        "fetch_scale": round(kf, 5), "write_scale": round(kw, 5),
+        "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+        "rowstats_source_sha256": sha,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 # --- GPU --------------------------------------------------------------------
@@ -98,9 +199,7 @@ def _traffic(launch_bytes):
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(ROWSTATS_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if t.get("rowstats_source_sha256") != sha:
+        if t.get("rowstats_source_sha256") != _rowstats_sha():
             return None
         return int(t["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -112,9 +211,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--cpu-sample", type=int, default=256, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="minimum wall time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a copy of known size (for counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter runs into the traffic file and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verification path shards by sequence with no "
               "exchange, so a multi-GPU figure is N independent copies of this one; "
@@ -124,7 +232,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         procs = max(1, min(16, os.cpu_count() or 1))
-        cpu = cpu_baseline(args.cpu_sample, procs)
+        cpu = cpu_baseline(args.cpu_sample, procs, args.cpu_seconds)
         print(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {procs} processes",
               file=sys.stderr, flush=True)
 
@@ -176,6 +284,8 @@ def main():
     total_ms = ev.elapsed_ms(2 * args.steps, 2 * args.steps + 1)
     k1_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]
     ev.close()
+    if args.calibration_copy:
+        calibration_copy(dev)
 
     ms_step = total_ms / args.steps
     k1_avg = sum(k1_ms) / len(k1_ms)
