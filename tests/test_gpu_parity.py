@@ -89,7 +89,9 @@ def test_single_small_parity(sv, case):
         ref = P.oracle_single(w, trial, trial * 7)
         P.compare(out, ref, SINGLE_KEYS, range(B), dt == "bf16", report)
     print(f"single {case[:4]}: {report}")
-    assert report["compared"] >= 0.8 * report["compared"] + report["exempt"] * 0
+    # near ties are rare on these laws: most sequences must be compared bit for bit
+    total = report["compared"] + report["exempt"]
+    assert report["exempt"] <= max(1, total // 10), report
 
 
 SMALL_HIER = [
