@@ -33,6 +33,8 @@ numerics   bf16/fp32 decode and the per-row target/draft distributions.
 rule       the accept test, the inverse-CDF draw, one verification chain.
 verify     batched single-stage and hierarchical (L_d -> L_i -> L_f) verify.
 blocktable paged-KV block-table / length rollback.
+lmhead     logits of a linear LM head (hidden . W^T, float64) fed to the
+           single-stage verify.
 
 Parity status: every function here is pinned by a CPU test (tests/test_oracle_*)
 except the 4x32 *constants* of Philox, which no library in the CPU container

@@ -27,11 +27,12 @@ def decode_bf16(bits):
 
 
 def decode(raw):
-    """Raw logits (uint16 holding bf16 bits, or float32) -> float64."""
+    """Raw logits (uint16 holding bf16 bits, float32, or float64 logits that an
+    LM head produced in float64) -> float64."""
     raw = np.asarray(raw)
     if raw.dtype == np.uint16:
         return decode_bf16(raw)
-    if raw.dtype == np.float32:
+    if raw.dtype in (np.float32, np.float64):
         return raw.astype(np.float64)
     raise TypeError(f"unsupported logit storage {raw.dtype}")
 

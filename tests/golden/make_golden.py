@@ -18,7 +18,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
-from oracle import philox, verify  # noqa: E402
+from oracle import lmhead, philox, verify  # noqa: E402
 
 
 def small_cases():
@@ -60,7 +60,31 @@ def philox_blocks():
     return rows
 
 
+def lmhead_cases():
+    """Small LM-head verify cases: hidden states and head as bf16 bit patterns."""
+    rng = np.random.default_rng(20251002)
+    cases = []
+    for idx, (B, k, d, V) in enumerate([(3, 4, 32, 41), (2, 2, 48, 29)]):
+        def bits(x):
+            return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        hd = bits(rng.normal(0, 1, (B, k, d)))
+        ht = bits(rng.normal(0, 1, (B, k + 1, d)))
+        w = bits(rng.normal(0, 0.3, (V, d)))
+        tokens = rng.integers(0, V, (B, k)).astype(np.int32)
+        temps = [1.0, 0.0, 0.8][:B]
+        seed, offset = 77 + idx, idx
+        r = lmhead.spec_verify_lmhead_single(hd, ht, w, tokens, np.array(temps), seed, offset)
+        cases.append(dict(B=B, k=k, d=d, V=V, temperature=temps, seed=seed, offset=offset,
+                          h_draft=hd.tolist(), h_target=ht.tolist(), w=w.tolist(),
+                          tokens=tokens.tolist(),
+                          expect=dict(accept_len=r["accept_len"].tolist(),
+                                      out_tokens=r["out_tokens"].tolist())))
+    return cases
+
+
 if __name__ == "__main__":
+    with open(os.path.join(HERE, "oracle_lmhead_cases.json"), "w") as f:
+        json.dump(lmhead_cases(), f)
     with open(os.path.join(HERE, "oracle_small_cases.json"), "w") as f:
         json.dump(small_cases(), f)
     with open(os.path.join(HERE, "oracle_philox_blocks.json"), "w") as f:

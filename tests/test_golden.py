@@ -5,7 +5,7 @@ import os
 
 import numpy as np
 
-from oracle import philox, verify
+from oracle import lmhead, philox, verify
 
 HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -35,3 +35,13 @@ def test_philox_blocks_reproduce():
         j, b, s, off = row["counter"]
         w = philox.block_words(np.uint64(j), b, s, off, row["seed"])
         assert [int(np.asarray(x)) for x in w] == row["words"]
+
+
+def test_lmhead_cases_reproduce():
+    for c in load("oracle_lmhead_cases.json"):
+        r = lmhead.spec_verify_lmhead_single(
+            np.array(c["h_draft"], dtype=np.uint16), np.array(c["h_target"], dtype=np.uint16),
+            np.array(c["w"], dtype=np.uint16), np.array(c["tokens"], dtype=np.int32),
+            np.array(c["temperature"]), c["seed"], c["offset"])
+        for key, val in c["expect"].items():
+            assert r[key].tolist() == val

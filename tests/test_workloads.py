@@ -52,3 +52,18 @@ def test_raw_view_round_trips():
     assert raw.dtype == np.uint16
     back = torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16)
     assert torch.equal(back, x)
+
+
+def test_lmhead_shapes_laws_and_drafts():
+    w = workloads.make_lmhead(6, 3, 700, 64, seed=(5, 1))
+    assert w["h_draft"].shape == (6, 3, 64) and w["h_target"].shape == (6, 4, 64)
+    assert w["w_vocab"].shape == (700, 64) and w["w_vocab"].dtype == torch.bfloat16
+    assert abs(float(w["w_vocab"].float().std()) - 0.02) < 0.002
+    assert abs(float(w["h_target"].float().std()) - 1.0) < 0.05
+    assert w["draft_tokens"].dtype == torch.int32
+    assert int(w["draft_tokens"].min()) >= 0 and int(w["draft_tokens"].max()) < 700
+    w2 = workloads.make_lmhead(6, 3, 700, 64, seed=(5, 1))
+    assert torch.equal(w["draft_tokens"], w2["draft_tokens"])
+    g = workloads.make_lmhead(4, 2, 300, 32, temps=(0.0,), seed=(5, 2))
+    logits = g["h_draft"].float() @ g["w_vocab"].float().T
+    assert torch.equal(g["draft_tokens"].long(), logits.argmax(-1))

@@ -30,6 +30,10 @@ hier          B=256, k=8, V=128256, bf16 L_d/L_i/L_f, std 3, alpha 0.85 (L_i vs
               of 16-slot blocks, context ~ U{512..4096}, length = context + k
 mixed_temp    B=32, k=5, V=151936, fp32, 4 * Student-t(3), alpha_b ~ U[0.3, 0.99],
               temperature_b uniform over {0, 0.7, 1.0}
+lmhead        B=128, k=4, d=4096, V=128256: bf16 hidden states of the draft and final
+              exits at k+1 positions, i.i.d. N(0, 1); a shared bf16 LM head W [V, d]
+              (one d-vector per vocabulary entry), i.i.d. N(0, 0.02^2); temperature 1;
+              drafts sampled from the draft exit's head logits at positions 0..k-1
 ===========  =====================================================================
 """
 
@@ -47,9 +51,10 @@ WORKLOADS = {
                  block_size=16, ctx=(512, 4096)),
     "mixed_temp": dict(kind="single", B=32, k=5, V=151936, dtype="f32", law="t3", scale=4.0,
                        alpha=(0.3, 0.99), temps=(0.0, 0.7, 1.0)),
+    "lmhead": dict(kind="lmhead", B=128, k=4, V=128256, d=4096, w_std=0.02, temps=(1.0,)),
 }
 
-_IDS = {"tiny": 1, "batched": 2, "hier": 3, "mixed_temp": 4}
+_IDS = {"tiny": 1, "batched": 2, "hier": 3, "mixed_temp": 4, "lmhead": 5}
 
 
 def _gen(device, *seed_parts):
@@ -168,6 +173,31 @@ def make_hier(B, k, V, dtype="bf16", law="normal", scale=3.0, alpha_i=0.85, alph
                 seq_lens=seq_lens.to(device), max_blocks=max_blocks)
 
 
+def make_lmhead(B, k, V, d, w_std=0.02, temps=(1.0,), seed=(0,), device="cpu"):
+    """LM-head inputs: hidden states h_draft [B, k, d] (the draft exit at the k
+    drafted positions), h_target [B, k+1, d], head w_vocab [V, d] (bf16), drafted
+    tokens sampled from the draft exit's head logits (float32, test side), and
+    temperatures."""
+    g = _gen(device, *seed)
+    hd = torch.randn((B, k + 1, d), generator=g, device=device).to(torch.bfloat16)
+    ht = torch.randn((B, k + 1, d), generator=g, device=device).to(torch.bfloat16)
+    w = torch.empty((V, d), dtype=torch.bfloat16, device=device)
+    for v0 in range(0, V, 16384):                     # bounded float32 temporaries
+        v1 = min(V, v0 + 16384)
+        w[v0:v1] = (torch.randn((v1 - v0, d), generator=g, device=device) * w_std).to(torch.bfloat16)
+    temperature = _temperatures(B, temps, g, device)
+    h_draft = hd[:, :k].contiguous()
+    tokens = torch.empty((B, k), dtype=torch.int32, device=device)
+    wf = w.float()
+    for b0 in range(0, B, 16):
+        b1 = min(B, b0 + 16)
+        logits = (h_draft[b0:b1].float().reshape(-1, d) @ wf.T).reshape(b1 - b0, k, V)
+        tokens[b0:b1] = sample_drafts(logits, temperature[b0:b1].cpu(), g)
+    del wf
+    return dict(kind="lmhead", B=B, k=k, V=V, d=d, dtype="bf16", h_draft=h_draft,
+                h_target=ht, w_vocab=w, draft_tokens=tokens, temperature=temperature)
+
+
 def make(name, trial=0, device="cpu"):
     """A named workload (see the module docstring) for a given trial index."""
     cfg = dict(WORKLOADS[name])
@@ -175,6 +205,8 @@ def make(name, trial=0, device="cpu"):
     seed = (_IDS[name], trial)
     if kind == "single":
         return make_single(seed=seed, device=device, **cfg)
+    if kind == "lmhead":
+        return make_lmhead(seed=seed, device=device, **cfg)
     return make_hier(seed=seed, device=device, **cfg)
 
 
