@@ -206,6 +206,72 @@ def _traffic(launch_bytes):
         return None
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_lmhead(args):
+    """The fused LM-head verify (B=128, k=4, d=4096, V=128256, bf16 hidden
+    states and head): one spec_verify_lmhead_single call per step.  Reports
+    verified draft tokens/s and the statistics GEMM's rate against the bf16
+    dense MFMA peak (2 * rows * V * d flops per launch, rows = B * (2k + 1))."""
+    import torch
+    import lossless_token_verification_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make("lmhead", 0, device=dev)
+    B, k, V, d = w["B"], w["k"], w["V"], w["d"]
+    ws = sv.alloc_workspace(sv.lmhead_workspace_bytes(B, k, V, d), dev)
+    rows = B * (2 * k + 1)
+    flops = 2.0 * rows * V * d
+    print(f"[bench] LM-head workload ready: {rows} rows, {flops / 1e12:.3f} TFLOP per GEMM",
+          file=sys.stderr, flush=True)
+    ev = HipEvents(2 * args.steps + 2)
+    bufs = {}
+
+    def step(i, events=None):
+        return sv.spec_verify_lmhead_single(w["h_draft"], w["h_target"], w["w_vocab"],
+                                            w["draft_tokens"], w["temperature"], seed=0,
+                                            offset=i, workspace=ws, events=events,
+                                            out=bufs.get("out"))
+
+    bufs["out"] = step(999999)
+    for i in range(args.warmup):
+        step(1000000 + i)
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev.hip.hipEventRecord(ev.ev[-2], stream)
+    for i in range(args.steps):
+        step(i, events=(ev.ev[2 * i].value, ev.ev[2 * i + 1].value))
+    ev.hip.hipEventRecord(ev.ev[-1], stream)
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(2 * args.steps, 2 * args.steps + 1)
+    g_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]
+    ev.close()
+    ms_step = total_ms / args.steps
+    g_avg = sum(g_ms) / len(g_ms)
+    tflops = flops / (g_avg / 1e3) / 1e12
+    line = {
+        "metric": "verified draft tokens/s, fused LM-head verify B=128 k=4 d=4096 V=128256 bf16",
+        "value": round(B * k / (ms_step / 1e3), 1),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "fused LM-head single-stage verify, B=128 k=4 d=4096 "
+                               "V=128256, bf16 hidden states and head", "B": B, "k": k,
+                   "d": d, "V": V},
+        "roofline": {"bound": "mfma", "kernel": "lmhead_gemm<stats>",
+                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops,
+                     "avg_launch_us": round(g_avg * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +285,9 @@ def main():
                     help="also run a copy of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into the traffic file and exit")
+    ap.add_argument("--path", choices=("hier", "lmhead"), default="hier",
+                    help="hier: the hierarchical verify + rollback step (default); lmhead: "
+                         "the fused LM-head verify")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -228,6 +297,10 @@ def main():
               "exchange, so a multi-GPU figure is N independent copies of this one; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.path == "lmhead":
+        bench_lmhead(args)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -97,6 +97,7 @@ extern "C" {
 /* Limits. */
 #define SV_MAX_DRAFT 63        /* k + 1 positions fit one 64-lane wavefront */
 #define SV_MAX_VOCAB (1 << 20) /* inverse-CDF tile sums stay in LDS          */
+#define SV_MAX_HIDDEN (1 << 16) /* hidden size of the LM-head path            */
 
 /* Device flags (spec_verify_device_status). */
 #define SV_FLAG_TOKEN_RANGE 1u /* a drafted token outside [0, V) was rejected        */
@@ -229,6 +230,46 @@ int32_t spec_verify_hier_rollback(const spec_verify_desc* desc, int32_t window,
                                   int32_t* freed_blocks, int32_t max_freed, int32_t* num_freed,
                                   void* workspace, size_t workspace_bytes,
                                   const spec_verify_diag* diag, void* hip_stream);
+
+/* Workspace bytes of spec_verify_lmhead_single (0 if desc or hidden is
+ * invalid). */
+size_t spec_verify_lmhead_workspace_bytes(const spec_verify_desc* desc, int32_t hidden);
+
+/* Single-stage verify whose logits come from a linear LM head shared by the
+ * draft and final exits: in an early-exit model each exit turns its hidden
+ * state into a token distribution (HiSpec summary, section 2
+ * "Kernmechanismus"); here q at drafted position j is the softmax of
+ * h_draft[b, j] . W^T and p the softmax of h_target[b, j] . W^T.  The rule is
+ * then exactly spec_verify_single's.  The logits are formed on the matrix
+ * cores (bf16 products, fp32 sums) and never stored: the softmax statistics
+ * and the logits at the drafted tokens are reduced from each output tile, and
+ * after the decisions only the rows each sequence draws from (p at the stop
+ * position and, for a correction, q there) are recomputed.
+ *   desc           dtype must be SV_DTYPE_BF16; vocab = V; row_stride = the
+ *                  head's row stride in elements (0 => hidden), a multiple
+ *                  of 8
+ *   hidden         d, a multiple of 64 in [64, SV_MAX_HIDDEN]
+ *   h_draft        [B, k, d]   device bf16, read-only (draft exit at the k
+ *                              drafted positions; may be NULL if k == 0)
+ *   h_target       [B, k+1, d] device bf16, read-only (final exit)
+ *   w_vocab        [V, row_stride] device bf16, read-only: row v is the
+ *                  d-vector of vocabulary entry v (a linear layer's weight)
+ *   the three must be 16-byte aligned; other arguments as for
+ *   spec_verify_single (diag.stats_begin/end bracket the statistics GEMM)
+ *   workspace      >= spec_verify_lmhead_workspace_bytes(desc, hidden): about
+ *                  B*(2k+1)*ceil(V/128)*16 bytes of tile statistics plus
+ *                  2*B*V*4 bytes of recomputed rows
+ * Errors as for spec_verify_single; a bf16 requirement or hidden size outside
+ * the limits is SV_ERR_UNSUPPORTED.
+ */
+int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
+                                  const void* h_draft, const void* h_target,
+                                  const void* w_vocab, const int32_t* draft_tokens,
+                                  const float* temperature, int32_t* accept_len,
+                                  int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                                  int32_t* packed_tokens, int32_t* cu_offsets, void* workspace,
+                                  size_t workspace_bytes, const spec_verify_diag* diag,
+                                  void* hip_stream);
 
 /* Synchronises hip_stream, then copies the device flags (SV_FLAG_*) of the
  * last verify call that used `workspace` into *flags_out (host). */

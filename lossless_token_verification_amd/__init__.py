@@ -36,13 +36,15 @@ SV_FLAG_TOKEN_RANGE = 1
 SV_FLAG_TEMPERATURE = 2
 MAX_DRAFT = 63
 MAX_VOCAB = 1 << 20
+MAX_HIDDEN = 1 << 16
 
 # Every symbol include/spec_verify.h declares.
 EXPORTED = (
     "spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
     "spec_verify_workspace_bytes", "spec_verify_validate", "spec_verify_single",
     "spec_verify_hier", "kv_blocktable_truncate", "spec_verify_hier_rollback",
-    "spec_verify_device_status",
+    "spec_verify_device_status", "spec_verify_lmhead_workspace_bytes",
+    "spec_verify_lmhead_single",
 )
 
 
@@ -101,6 +103,11 @@ def library():
     lib.kv_blocktable_truncate.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P]
     lib.spec_verify_device_status.restype = i32
     lib.spec_verify_device_status.argtypes = [P, ctypes.POINTER(u32), P]
+    lib.spec_verify_lmhead_workspace_bytes.restype = sz
+    lib.spec_verify_lmhead_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i32]
+    lib.spec_verify_lmhead_single.restype = i32
+    lib.spec_verify_lmhead_single.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P, P, P,
+                                              P, P, P, P, sz, ctypes.POINTER(Diag), P]
     _lib = lib
     return lib
 
@@ -245,6 +252,57 @@ def spec_verify_single(draft_logits, target_logits, draft_tokens, temperature=No
     _check(lib.spec_verify_single(
         ctypes.byref(desc), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+        _ptr(out["num_emitted"]), _ptr(out["num_drop"]), _ptr(out.get("packed_tokens")),
+        _ptr(out.get("cu_offsets")), _ptr(ws), ws.numel(),
+        ctypes.byref(dg) if dg is not None else None, _stream(dev)))
+    return out
+
+
+def lmhead_workspace_bytes(batch, num_draft, vocab, hidden, row_stride=0):
+    desc = make_desc(batch, num_draft, vocab, SV_DTYPE_BF16, row_stride)
+    return library().spec_verify_lmhead_workspace_bytes(ctypes.byref(desc), hidden)
+
+
+def _bf16_rows(t, name, shape, device):
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous() or \
+            t.device != device:
+        raise ValueError(f"{name} must be a contiguous bf16 {list(shape)} tensor on one device")
+
+
+def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperature=None, *,
+                              seed=0, offset=0, packed=False, diag=False, workspace=None,
+                              events=None, out=None):
+    """Single-stage verify through a linear LM head W [V, d] (one d-vector per
+    vocabulary entry): q from h_draft [B, k, d], p from h_target [B, k+1, d].
+    Returns the same dict as spec_verify_single.  ``out`` reuses the output
+    tensors of an earlier call with the same shapes.  Asynchronous."""
+    lib = library()
+    B, k1, d = h_target.shape
+    k = k1 - 1
+    V = w_vocab.shape[0]
+    dev = h_target.device
+    _bf16_rows(h_target, "h_target", (B, k + 1, d), dev)
+    _bf16_rows(h_draft, "h_draft", (B, k, d), dev)
+    if w_vocab.dim() != 2 or w_vocab.shape[1] != d or w_vocab.dtype != torch.bfloat16 or \
+            w_vocab.stride(1) != 1 or w_vocab.device != dev:
+        raise ValueError("w_vocab must be a bf16 [V, d] tensor, contiguous along d")
+    _prep_common(draft_tokens, temperature, B, k, dev)
+    desc = make_desc(B, k, V, SV_DTYPE_BF16, w_vocab.stride(0) if V > 1 else d, seed, offset)
+    need = lib.spec_verify_lmhead_workspace_bytes(ctypes.byref(desc), d)
+    if need == 0:
+        raise SpecVerifyError(SV_ERR_UNSUPPORTED, "unsupported LM-head shape")
+    ws = workspace if workspace is not None else alloc_workspace(need, dev)
+    if out is None:
+        out = dict(accept_len=_int_out((B,), dev), out_tokens=_int_out((B, k + 1), dev),
+                   num_emitted=_int_out((B,), dev), num_drop=_int_out((B,), dev))
+        if packed:
+            out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
+            out["cu_offsets"] = _int_out((B + 1,), dev)
+    out["workspace"] = ws
+    dg = _make_diag(diag, events, B, k, dev, out)
+    _check(lib.spec_verify_lmhead_single(
+        ctypes.byref(desc), d, _ptr(h_draft), _ptr(h_target), _ptr(w_vocab),
+        _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
         _ptr(out["num_emitted"]), _ptr(out["num_drop"]), _ptr(out.get("packed_tokens")),
         _ptr(out.get("cu_offsets")), _ptr(ws), ws.numel(),
         ctypes.byref(dg) if dg is not None else None, _stream(dev)))

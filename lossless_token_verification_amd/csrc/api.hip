@@ -275,6 +275,210 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   return SV_OK;
 }
 
+// Workspace and launch plan of the LM-head path.
+struct LmPlan {
+  int64_t M = 0;          // GEMM rows: B*k draft rows, then B*(k+1) target rows
+  int n_tiles = 0;        // vocabulary tiles of the GEMM
+  int nt = 0, ns = 0;     // draw tiles per recomputed row and slices per sequence
+  int64_t ldw = 0, ldo = 0;
+  size_t seq_bytes = 0, tile_bytes = 0, part_bytes = 0, merged_bytes = 0, gath_bytes = 0,
+         stop_bytes = 0, rows_bytes = 0, ws_bytes = 0;
+};
+
+size_t pad256(size_t n) { return (n + 255) / 256 * 256; }
+
+int32_t make_lm_plan(const spec_verify_desc* d, int32_t hidden, LmPlan* p) {
+  if (!d) return fail(SV_ERR_INVALID_ARG, "desc is NULL");
+  if (d->reserved != 0) return fail(SV_ERR_INVALID_ARG, "desc.reserved must be 0");
+  if (d->batch < 0) return fail(SV_ERR_INVALID_ARG, "batch < 0");
+  if (d->num_draft < 0) return fail(SV_ERR_INVALID_ARG, "num_draft < 0");
+  if (d->num_draft > SV_MAX_DRAFT)
+    return fail(SV_ERR_UNSUPPORTED, "num_draft > " + std::to_string(SV_MAX_DRAFT));
+  if (d->vocab < 1) return fail(SV_ERR_INVALID_ARG, "vocab < 1");
+  if (d->vocab > SV_MAX_VOCAB)
+    return fail(SV_ERR_UNSUPPORTED, "vocab > " + std::to_string(SV_MAX_VOCAB));
+  if (d->dtype != SV_DTYPE_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "the LM-head path takes bf16 hidden states and head");
+  if (hidden < sv::kGemmKT || hidden % sv::kGemmKT != 0 || hidden > SV_MAX_HIDDEN)
+    return fail(SV_ERR_UNSUPPORTED, "hidden must be a multiple of 64 in [64, " +
+                                        std::to_string(SV_MAX_HIDDEN) + "]");
+  const int64_t ldw = d->row_stride == 0 ? hidden : d->row_stride;
+  if (ldw < hidden) return fail(SV_ERR_INVALID_ARG, "row_stride < hidden");
+  if (ldw % 8 != 0) return fail(SV_ERR_MISALIGNED, "row_stride not a multiple of 8");
+  if (ldw > (int64_t(1) << 40)) return fail(SV_ERR_INVALID_ARG, "row_stride too large");
+  const int64_t B = d->batch, k = d->num_draft;
+  p->M = B * (2 * k + 1);
+  p->n_tiles = (d->vocab + sv::kGemmNT - 1) / sv::kGemmNT;
+  if (p->M > INT32_MAX / 2 || p->M * p->n_tiles > INT32_MAX)
+    return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
+  const int te = sv::tile_elems(SV_DTYPE_F32);   // draws read fp32 recomputed rows
+  p->nt = (d->vocab + te - 1) / te;
+  p->ns = (p->nt + sv::kTilesPerSlice - 1) / sv::kTilesPerSlice;
+  p->ldw = ldw;
+  p->ldo = (static_cast<int64_t>(d->vocab) + 3) / 4 * 4;
+  p->seq_bytes = pad256(static_cast<size_t>(B) * 5 * sizeof(int32_t));
+  p->tile_bytes = pad256(static_cast<size_t>(B) * 2 * p->nt * sizeof(float));
+  p->part_bytes = pad256(static_cast<size_t>(p->M) * p->n_tiles * sizeof(sv::Partial));
+  p->merged_bytes = pad256(static_cast<size_t>(p->M) * sizeof(sv::Partial));
+  p->gath_bytes = pad256(static_cast<size_t>(p->M) * sizeof(float));
+  p->stop_bytes = pad256(static_cast<size_t>(B) * 2 * sizeof(int32_t));
+  p->rows_bytes = static_cast<size_t>(B) * 2 * p->ldo * sizeof(float);
+  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes + p->part_bytes +
+                p->merged_bytes + p->gath_bytes + p->stop_bytes + p->rows_bytes;
+  return SV_OK;
+}
+
+int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_draft,
+                   const void* h_target, const void* w_vocab, const int32_t* tokens,
+                   const float* temperature, int32_t* accept_len, int32_t* out_tokens,
+                   int32_t* num_emitted, int32_t* num_drop, int32_t* packed,
+                   int32_t* cu_offsets, void* workspace, size_t workspace_bytes,
+                   const spec_verify_diag* diag, void* hip_stream) {
+  LmPlan p;
+  SV_TRY(make_lm_plan(desc, hidden, &p));
+  const int B = desc->batch, k = desc->num_draft;
+  const bool any = B > 0;
+  if (any) {
+    if (k > 0 && !h_draft) return fail(SV_ERR_INVALID_ARG, "h_draft is NULL");
+    if (!h_target) return fail(SV_ERR_INVALID_ARG, "h_target is NULL");
+    if (!w_vocab) return fail(SV_ERR_INVALID_ARG, "w_vocab is NULL");
+    if ((k > 0 && !aligned_to(h_draft, 16)) || !aligned_to(h_target, 16) ||
+        !aligned_to(w_vocab, 16))
+      return fail(SV_ERR_MISALIGNED, "hidden states and head must be 16-byte aligned");
+  }
+  SV_TRY(check_i32(tokens, any && k > 0, "draft_tokens"));
+  if (temperature && !aligned_to(temperature, 4))
+    return fail(SV_ERR_MISALIGNED, "temperature not 4-byte aligned");
+  SV_TRY(check_i32(accept_len, any, "accept_len"));
+  SV_TRY(check_i32(out_tokens, any, "out_tokens"));
+  SV_TRY(check_i32(num_emitted, any, "num_emitted"));
+  SV_TRY(check_i32(num_drop, false, "num_drop"));
+  SV_TRY(check_i32(packed, false, "packed_tokens"));
+  SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
+  if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
+  SV_TRY(check_diag(diag));
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned_to(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < p.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, needs " + std::to_string(p.ws_bytes));
+  if (!any) return SV_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = ws + off;
+    off += n;
+    return q;
+  };
+  uint32_t* flags = reinterpret_cast<uint32_t*>(take(sv::kFlagsBytes));
+  int32_t* seqw = reinterpret_cast<int32_t*>(take(p.seq_bytes));
+  float* tsum = reinterpret_cast<float*>(take(p.tile_bytes));
+  sv::Partial* part = reinterpret_cast<sv::Partial*>(take(p.part_bytes));
+  sv::Partial* merged = reinterpret_cast<sv::Partial*>(take(p.merged_bytes));
+  float* gath = reinterpret_cast<float*>(take(p.gath_bytes));
+  int32_t* stop_rows = reinterpret_cast<int32_t*>(take(p.stop_bytes));
+  float* rows = reinterpret_cast<float*>(take(p.rows_bytes));
+  hipError_t err;
+
+  sv::GemmArgs g{};
+  g.a_draft = static_cast<const uint16_t*>(h_draft);
+  g.a_target = static_cast<const uint16_t*>(h_target);
+  g.w = static_cast<const uint16_t*>(w_vocab);
+  g.ldw = p.ldw;
+  g.M = static_cast<int32_t>(p.M);
+  g.m_draft = B * k;
+  g.V = desc->vocab;
+  g.d = hidden;
+  g.B = B;
+  g.k = k;
+  g.n_tiles = p.n_tiles;
+  g.tokens = tokens;
+  g.temperature = temperature;
+  g.partials = part;
+  g.gath = gath;
+  if (diag && diag->stats_begin) {
+    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
+    if (err != hipSuccess) return device_error(err, "event record");
+  }
+  err = sv::launch_lmhead_stats(g, st);
+  if (err != hipSuccess) return device_error(err, "LM-head statistics launch");
+  if (diag && diag->stats_end) {
+    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
+    if (err != hipSuccess) return device_error(err, "event record");
+  }
+
+  sv::MergeArgs ma{part, merged, g.M, p.n_tiles, seqw, 3 * B, flags};
+  err = sv::launch_merge(ma, st);
+  if (err != hipSuccess) return device_error(err, "merge launch");
+
+  sv::VerifyArgs va{};
+  va.hier = 0;
+  va.B = B;
+  va.k = k;
+  va.V = desc->vocab;
+  va.dtype = SV_DTYPE_F32;   // the draws read fp32 recomputed rows
+  va.nc = 1;
+  va.window = 1;
+  va.nt = p.nt;
+  va.ns = 1;                 // decisions: one workgroup per sequence
+  va.tps = sv::kTilesPerSlice;
+  va.ld = p.ldo;
+  va.exit_row0[0] = 0;
+  va.exit_row0[1] = B * k;
+  va.partials = merged;
+  for (int s = 0; s < 2; ++s) {
+    va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
+    va.cnt[s] = seqw + s * B;
+  }
+  va.done = seqw + 2 * B;
+  va.ytok = seqw + 3 * B;
+  va.ztok = seqw + 4 * B;
+  va.tokens = tokens;
+  va.temperature = temperature;
+  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  va.offset = desc->offset;
+  va.accept_len = accept_len;
+  va.out_tokens = out_tokens;
+  va.num_emitted = num_emitted;
+  va.num_drop = num_drop;
+  va.diag_uniforms = diag ? diag->uniforms : nullptr;
+  va.diag_probs = diag ? diag->probs : nullptr;
+  va.diag_draws = diag ? diag->draws : nullptr;
+  va.flags = flags;
+  va.gath = gath;
+  va.decide_only = 1;
+  va.stop_rows = stop_rows;
+  err = sv::launch_verify(va, st);
+  if (err != hipSuccess) return device_error(err, "decision launch");
+
+  sv::GemmArgs r = g;
+  r.a_rows = stop_rows;
+  r.M = 2 * B;
+  r.out = rows;
+  r.ldo = p.ldo;
+  r.partials = nullptr;
+  r.gath = nullptr;
+  err = sv::launch_lmhead_rows(r, st);
+  if (err != hipSuccess) return device_error(err, "LM-head row recompute launch");
+
+  va.ns = p.ns;
+  va.decide_only = 0;
+  va.draw_rows = rows;
+  va.draw_ld = p.ldo;
+  err = sv::launch_verify(va, st);
+  if (err != hipSuccess) return device_error(err, "draw launch");
+
+  if (packed) {
+    sv::PackArgs pa{B, k, out_tokens, num_emitted, packed, cu_offsets};
+    err = sv::launch_pack(pa, st);
+    if (err != hipSuccess) return device_error(err, "pack launch");
+  }
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -369,6 +573,27 @@ int32_t spec_verify_hier_rollback(const spec_verify_desc* desc, int32_t window,
   return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
                     accept_len_final, out_tokens, num_emitted, num_drop, nullptr, nullptr,
                     workspace, workspace_bytes, diag, hip_stream, &kv);
+}
+
+size_t spec_verify_lmhead_workspace_bytes(const spec_verify_desc* desc, int32_t hidden) {
+  LmPlan p;
+  const std::string keep = g_last_error;
+  const int32_t s = make_lm_plan(desc, hidden, &p);
+  g_last_error = keep;
+  return s == SV_OK ? p.ws_bytes : 0;
+}
+
+int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
+                                  const void* h_draft, const void* h_target,
+                                  const void* w_vocab, const int32_t* draft_tokens,
+                                  const float* temperature, int32_t* accept_len,
+                                  int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                                  int32_t* packed_tokens, int32_t* cu_offsets, void* workspace,
+                                  size_t workspace_bytes, const spec_verify_diag* diag,
+                                  void* hip_stream) {
+  return run_lmhead(desc, hidden, h_draft, h_target, w_vocab, draft_tokens, temperature,
+                    accept_len, out_tokens, num_emitted, num_drop, packed_tokens, cu_offsets,
+                    workspace, workspace_bytes, diag, hip_stream);
 }
 
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream) {

@@ -1,0 +1,381 @@
+// LM-head path: the logits of the draft and final exits are never written to
+// memory.  A bf16 GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16) multiplies
+// the exits' hidden states by the shared head W [V, d] and reduces each
+// 128 x 128 output tile in its epilogue to the per-(row, vocabulary tile)
+// softmax partials the verification launch merges, plus the logit at each
+// row's drafted token.  After the decisions, the same GEMM recomputes only
+// the two rows each sequence draws from (the target row at the stop position
+// and, for a correction, the draft row there).
+//
+// In an early-exit model each exit turns its hidden state into a token
+// distribution (HiSpec summary, section 2 "Kernmechanismus"); with a linear
+// head the distribution is the softmax of hidden . W^T.
+//
+// Tiling (256 threads, 2 x 2 wavefronts of 64 x 64 outputs each): both
+// operands are K-contiguous (hidden states [rows, d], head [V, d]), so each
+// 64-element K step of the A and W tiles is copied to LDS with 16-byte loads
+// and stores, and every MFMA operand is one 16-byte LDS read per lane.  Global
+// loads of step k+1 are issued before the MFMAs of step k (two LDS buffers,
+// one barrier per step).  Workgroup i runs on XCD i % 8; the M tiles of one
+// vocabulary tile are consecutive on one XCD, so the W tile is fetched from
+// HBM once and served to the other M tiles from that XCD's L2.
+#include <algorithm>
+
+#include "sv_common.h"
+
+namespace sv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int WM = 2, WN = 2;          // wavefront grid of a workgroup
+constexpr int FM = 2, FN = 2;          // 32 x 32 MFMA tiles per wavefront
+constexpr int GT = WM * WN * kWave;    // threads per workgroup
+constexpr int MT = WM * FM * 32;
+constexpr int NT = WN * FN * 32;
+constexpr int KT = kGemmKT;
+constexpr int LROW = KT + 8;           // bf16 per LDS row (16-byte pad against bank conflicts)
+constexpr int VPR = KT / 8;            // 16-byte vectors per tile row
+constexpr int A_PER = MT * VPR / GT;   // A vectors each thread copies per step
+constexpr int B_PER = NT * VPR / GT;
+static_assert(MT == kGemmMT && NT == kGemmNT, "tile sizes");
+static_assert(GT == kThreads, "one workgroup size");
+static_assert(MT * VPR % GT == 0 && NT * VPR % GT == 0, "copy slots");
+
+struct TileShared {
+  alignas(16) uint16_t a[2][MT * LROW];
+  alignas(16) uint16_t b[2][NT * LROW];
+};
+
+struct EpiShared {
+  float m[WN][MT];
+  int i[WN][MT];
+  float s[WN][MT];
+  float rs[MT];     // log2(e) / temperature of the row (0: greedy)
+  int tok[MT];      // drafted token of the row (-1: none); rows mode: source row
+  float rmax[MT];
+  int ridx[MT];
+};
+
+__device__ __forceinline__ const uint16_t* a_row(const GemmArgs& a, int g) {
+  return g < a.m_draft ? a.a_draft + static_cast<int64_t>(g) * a.d
+                       : a.a_target + static_cast<int64_t>(g - a.m_draft) * a.d;
+}
+
+// Sequence and drafted token of GEMM row g (stats numbering).
+__device__ __forceinline__ void row_meta(const GemmArgs& a, int g, int& b, int& tok) {
+  if (g < a.m_draft) {
+    b = g / a.k;
+    tok = a.tokens[g];
+  } else {
+    const int r = g - a.m_draft;
+    b = r / (a.k + 1);
+    const int j = r - b * (a.k + 1);
+    tok = j < a.k ? a.tokens[static_cast<int64_t>(b) * a.k + j] : -1;
+  }
+}
+
+template <bool ROWS>
+__global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
+  __shared__ TileShared sm;
+  __shared__ EpiShared ep;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / WN, wn = wave - wm * WN;
+  const int nM = (a.M + MT - 1) / MT;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int ntile = (local / nM) * 8 + xcd;
+  const int mtile = local - (local / nM) * nM;
+  if (ntile >= a.n_tiles) return;   // padding of the grid to a multiple of 8 tiles
+  const int m0 = mtile * MT, n0 = ntile * NT;
+
+  // copy slots of this thread: tile row v / VPR, 16-byte vector v % VPR
+  const uint16_t* ap[A_PER];
+  const uint16_t* bp[B_PER];
+  int aoff[A_PER], boff[B_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
+    int g = m0 + r;
+    bool ok = g < a.M;
+    if (ROWS && ok) {
+      g = a.a_rows[g];
+      ok = g >= 0;
+    }
+    ap[i] = ok ? a_row(a, g) + kv * 8 : nullptr;
+    aoff[i] = r * LROW + kv * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
+    const int n = n0 + r;
+    bp[i] = n < a.V ? a.w + static_cast<int64_t>(n) * a.ldw + kv * 8 : nullptr;
+    boff[i] = r * LROW + kv * 8;
+  }
+  u32x4 ra[A_PER], rb[B_PER];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i)
+      ra[i] = ap[i] ? *reinterpret_cast<const u32x4*>(ap[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i)
+      rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) *reinterpret_cast<u32x4*>(&sm.a[buf][aoff[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) *reinterpret_cast<u32x4*>(&sm.b[buf][boff[i]]) = rb[i];
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[fm][fn][q] = 0.0f;
+
+  const int nK = a.d / KT;
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nK; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nK) gload((kt + 1) * KT);
+#pragma unroll
+    for (int ks = 0; ks < KT / 16; ++ks) {
+      bf16x8 af[FM], bf[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * FM * 32 + fm * 32 + frow;
+        af[fm] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&sm.a[cur][r * LROW + ks * 16 + fk]));
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int r = wn * FN * 32 + fn * 32 + frow;
+        bf[fn] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&sm.b[cur][r * LROW + ks * 16 + fk]));
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+    }
+    if (kt + 1 < nK) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Output element (fm, fn, q) of this lane: row wm*64 + fm*32 + (q/4)*8 +
+  // h*4 + q%4, column wn*64 + fn*32 + c32 (h = lane / 32, c32 = lane % 32).
+  const int h = lane >> 5, c32 = lane & 31;
+  auto row_of = [&](int fm, int q) { return wm * FM * 32 + fm * 32 + (q >> 2) * 8 + h * 4 + (q & 3); };
+  auto col_of = [&](int fn) { return n0 + wn * FN * 32 + fn * 32 + c32; };
+
+  if (ROWS) {
+    if (tid < MT) ep.tok[tid] = m0 + tid < a.M ? a.a_rows[m0 + tid] : -1;
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rl = row_of(fm, q);
+        if (ep.tok[rl] < 0) continue;
+        float* orow = a.out + static_cast<int64_t>(m0 + rl) * a.ldo;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = col_of(fn);
+          if (col < a.V) orow[col] = acc[fm][fn][q];
+        }
+      }
+    return;
+  }
+
+  if (tid < MT) {
+    const int g = m0 + tid;
+    float s = 0.0f;
+    int tok = -1;
+    if (g < a.M) {
+      int b;
+      row_meta(a, g, b, tok);
+      const float tau = a.temperature ? a.temperature[b] : 1.0f;
+      const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
+      s = greedy ? 0.0f : kLog2e / tau;
+    }
+    ep.rs[tid] = s;
+    ep.tok[tid] = tok;
+  }
+  __syncthreads();
+
+  // pass 1: (max, lowest column) of each row over the tile
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      float m = -INFINITY;
+      int idx = 0x7fffffff;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = col_of(fn);
+        const float v = acc[fm][fn][q];
+        if (col < a.V && v > m) {
+          m = v;
+          idx = col;
+        }
+      }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) {
+        const float om = __shfl_xor(m, o, kWave);
+        const int oi = __shfl_xor(idx, o, kWave);
+        if (om > m || (om == m && oi < idx)) {
+          m = om;
+          idx = oi;
+        }
+      }
+      if (c32 == 0) {
+        const int rl = row_of(fm, q);
+        ep.m[wn][rl] = m;
+        ep.i[wn][rl] = idx;
+      }
+    }
+  __syncthreads();
+  if (tid < MT) {
+    float m = ep.m[0][tid];
+    int idx = ep.i[0][tid];
+#pragma unroll
+    for (int w = 1; w < WN; ++w) {
+      if (ep.m[w][tid] > m || (ep.m[w][tid] == m && ep.i[w][tid] < idx)) {
+        m = ep.m[w][tid];
+        idx = ep.i[w][tid];
+      }
+    }
+    ep.rmax[tid] = m;
+    ep.ridx[tid] = idx;
+  }
+  __syncthreads();
+
+  // pass 2: sum of 2^(l * s - c), c = max * s, and the drafted token's logit
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int rl = row_of(fm, q);
+      const float s = ep.rs[rl];
+      const float nc = -(ep.rmax[rl] * s);
+      const int tok = ep.tok[rl];
+      float sum = 0.0f;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = col_of(fn);
+        const float v = acc[fm][fn][q];
+        if (col < a.V && s > 0.0f) sum += __builtin_amdgcn_exp2f(fmaf(v, s, nc));
+        if (col == tok) a.gath[m0 + rl] = v;
+      }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+      if (c32 == 0) ep.s[wn][rl] = sum;
+    }
+  __syncthreads();
+  if (tid < MT && m0 + tid < a.M) {
+    Partial p;
+    if (ep.rs[tid] > 0.0f) {
+      double S = 0.0;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) S += static_cast<double>(ep.s[w][tid]);
+      p.key = ep.rmax[tid] * ep.rs[tid];
+      p.amax = -1;
+      p.S = S;
+    } else {
+      p.key = ep.rmax[tid];
+      p.amax = ep.ridx[tid];
+      p.S = 0.0;
+    }
+    a.partials[static_cast<int64_t>(m0 + tid) * a.n_tiles + ntile] = p;
+  }
+}
+
+// One wavefront per row: merge the row's n partials (a greedy row's partials
+// carry an argmax >= 0, a sampled row's -1).  The first workgroups also clear
+// the counters of the verification launches.
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
+    if (i < a.n_clear) a.clear_words[i] = 0;
+    if (i == 0) a.flags[0] = 0u;
+  }
+  const int row = blockIdx.x * kWaves + tid / kWave;
+  if (row >= a.rows) return;
+  const Partial* pp = a.in + static_cast<int64_t>(row) * a.n;
+  const bool greedy = pp[0].amax >= 0;
+  Partial out;
+  if (greedy) {
+    float m = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int c = lane; c < a.n; c += kWave) {
+      const Partial q = pp[c];
+      if (q.key > m || (q.key == m && q.amax < idx)) {
+        m = q.key;
+        idx = q.amax;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, kWave);
+      const int oi = __shfl_xor(idx, o, kWave);
+      if (om > m || (om == m && oi < idx)) {
+        m = om;
+        idx = oi;
+      }
+    }
+    out.key = m;
+    out.amax = idx;
+    out.S = 0.0;
+  } else {
+    float cm = -INFINITY;
+    for (int c = lane; c < a.n; c += kWave) cm = fmaxf(cm, pp[c].key);
+    cm = wave_max(cm);
+    double S = 0.0;
+    for (int c = lane; c < a.n; c += kWave) {
+      const Partial q = pp[c];
+      if (q.S > 0.0) S += q.S * exp2(static_cast<double>(q.key) - static_cast<double>(cm));
+    }
+    S = wave_sum(S);
+    out.key = cm;
+    out.amax = -1;
+    out.S = S;
+  }
+  if (lane == 0) a.out[row] = out;
+}
+
+unsigned gemm_grid(const GemmArgs& a) {
+  const unsigned nM = static_cast<unsigned>((a.M + MT - 1) / MT);
+  const unsigned nN8 = static_cast<unsigned>((a.n_tiles + 7) / 8) * 8u;
+  return nM * nN8;
+}
+
+}  // namespace
+
+hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(lmhead_gemm<false>, dim3(gemm_grid(a)), dim3(GT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(lmhead_gemm<true>, dim3(gemm_grid(a)), dim3(GT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  const int64_t by_rows = (static_cast<int64_t>(a.rows) + kWaves - 1) / kWaves;
+  const int64_t by_clear = (static_cast<int64_t>(a.n_clear) + kThreads - 1) / kThreads;
+  const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::max(by_rows, by_clear)));
+  hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -90,6 +90,16 @@ struct VerifyArgs {
   double* diag_probs;
   double* diag_draws;
   uint32_t* flags;
+  // LM-head path: logits at the drafted tokens come from `gath` (one per row,
+  // NULL: read from the logit rows), the draws read the recomputed stopped
+  // rows of `draw_rows` ([2B, draw_ld] fp32: p row 2b, q row 2b + 1), and a
+  // first pass with `decide_only` writes each sequence's stopped rows to
+  // `stop_rows` (greedy sequences are finished there).
+  const float* gath;
+  const float* draw_rows;
+  int64_t draw_ld;
+  int32_t decide_only;
+  int32_t* stop_rows;
   // optional paged-KV rollback of every sequence once its result is known
   int32_t* kv_table;       // [B, kv_max_blocks] or NULL
   int32_t* kv_lens;        // [B]
@@ -114,6 +124,50 @@ struct KvArgs {
   int32_t* freed;
   int32_t* num_freed;
 };
+
+// LM-head GEMM: logits[r, v] = sum_i A[r, i] * W[v, i] for bf16 A rows
+// (hidden states) and a bf16 head W [V, ldw], fp32 accumulation on MFMA.
+// Row r of A is draft row r (r < m_draft: a_draft + r * d) or target row
+// r - m_draft (a_target); with `a_rows`, GEMM row r takes A row a_rows[r]
+// (-1: the row is skipped).  Epilogues:
+//  - stats: partial softmax statistics of every (row, N tile), in the Partial
+//    format of the row-statistics kernel, and the logit at the row's drafted
+//    token (draft row b*k + j and target row b*(k+1) + j, j < k, hold token
+//    tokens[b*k + j]);
+//  - rows: the fp32 logits themselves, out[r * ldo + v].
+struct GemmArgs {
+  const uint16_t* a_draft;
+  const uint16_t* a_target;
+  const int32_t* a_rows;
+  const uint16_t* w;
+  int64_t ldw;
+  int32_t M, m_draft, V, d, B, k;
+  int32_t n_tiles;          // N tiles of the grid (vocabulary tiles)
+  const int32_t* tokens;
+  const float* temperature;
+  Partial* partials;        // [M, n_tiles]
+  float* gath;              // [M]
+  float* out;               // [M, ldo]
+  int64_t ldo;
+};
+// Merges the n partials of each of `rows` rows into one (nc = 1 format).
+// The first workgroups also zero `clear_words` and the flag word (the
+// counters of the verification launches that follow).
+struct MergeArgs {
+  const Partial* in;
+  Partial* out;
+  int32_t rows, n;
+  int32_t* clear_words;
+  int32_t n_clear;
+  uint32_t* flags;
+};
+constexpr int kGemmMT = 128;   // rows per GEMM workgroup tile
+constexpr int kGemmNT = 128;   // vocabulary entries per GEMM workgroup tile
+constexpr int kGemmKT = 64;    // hidden elements per pipeline step
+
+hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st);
+hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);

@@ -405,6 +405,10 @@ struct SeqCtx {
 
   __device__ int positions(int e) const { return e == 0 ? k : k + 1; }
 
+  __device__ int64_t row_index(int e, int j) const {
+    return a.exit_row0[e] + static_cast<int64_t>(b) * positions(e) + j;
+  }
+
   __device__ const char* row_ptr(int e, int j) const {
     return static_cast<const char*>(a.exit_ptr[e]) +
            (static_cast<int64_t>(b) * positions(e) + j) * a.ld * RowT<DT>::ES;
@@ -617,8 +621,8 @@ struct SeqCtx {
           pj = valid && x == sm.st[pe][j].amax ? 1.0 : 0.0;
           qj = valid && x == sm.st[qe][j].amax ? 1.0 : 0.0;
         } else if (valid) {
-          const float lp = load_elem(row_ptr(pe, j), x, DT);
-          const float lq = load_elem(row_ptr(qe, j), x, DT);
+          const float lp = a.gath ? a.gath[row_index(pe, j)] : load_elem(row_ptr(pe, j), x, DT);
+          const float lq = a.gath ? a.gath[row_index(qe, j)] : load_elem(row_ptr(qe, j), x, DT);
           const float ep = __builtin_amdgcn_exp2f(fmaf(lp, s, -sm.st[pe][j].key));
           const float eq = __builtin_amdgcn_exp2f(fmaf(lq, s, -sm.st[qe][j].key));
           pj = static_cast<double>(ep) / sm.st[pe][j].S;
@@ -741,8 +745,16 @@ __device__ int draw_finish(SeqCtx<DT>& cx, int stage, const char* pr, const char
 template <int DT>
 __device__ int sliced_draw(SeqCtx<DT>& cx, int slice, int qe, int pe, int apos, bool has_q,
                            int stage, float v, const RowStat& ps, const RowStat& qs) {
-  const char* pr = cx.row_ptr(pe, apos);
-  const char* qr = has_q ? cx.row_ptr(qe, apos) : nullptr;
+  const char* pr;
+  const char* qr;
+  if (cx.a.draw_rows) {   // LM-head path: the recomputed rows of this sequence
+    const float* base = cx.a.draw_rows + static_cast<int64_t>(cx.b) * 2 * cx.a.draw_ld;
+    pr = reinterpret_cast<const char*>(base);
+    qr = has_q ? reinterpret_cast<const char*>(base + cx.a.draw_ld) : nullptr;
+  } else {
+    pr = cx.row_ptr(pe, apos);
+    qr = has_q ? cx.row_ptr(qe, apos) : nullptr;
+  }
   if (!draw_slice<DT>(cx, slice, stage, pr, qr, has_q, ps, qs)) return -2;
   return draw_finish<DT>(cx, stage, pr, qr, has_q, ps, qs, v);
 }
@@ -791,6 +803,18 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int w, VerifyShared& sm
     a1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1, first);
     a2p = a1;
     v1 = sm.vs[a1];
+  }
+  if (a.decide_only) {
+    // LM-head first pass: name the rows to recompute (target row a1, and the
+    // draft row a1 for a correction); greedy sequences end here
+    if (!first) return;
+    if (tid == 0) {
+      const bool draws = !cx.greedy;
+      a.stop_rows[2 * b] = draws ? static_cast<int32_t>(cx.row_index(1, a1)) : -1;
+      a.stop_rows[2 * b + 1] = draws && a1 < k ? static_cast<int32_t>(cx.row_index(0, a1)) : -1;
+    }
+    if (cx.greedy) cx.write_outputs(a1 + 1, sm.st[1][a1].amax, a1, -1);
+    return;
   }
   if (first && a.diag_draws && tid < 8) {
     // draw diagnostics of the draws that do not happen (the others are written

@@ -16,6 +16,7 @@ import numpy as np
 import torch
 
 import workloads
+from oracle import lmhead as olm
 from oracle import verify as ov
 
 RATIO_EPS = 1e-5
@@ -40,6 +41,13 @@ def oracle_hier(w, seed, offset, window, sequences=None):
     return ov.spec_verify_hier(raw(w["ld_logits"]), raw(w["li_logits"]), raw(w["lf_logits"]),
                                w["draft_tokens"].cpu().numpy(), temps, seed, offset, window,
                                sequences=sequences)
+
+
+def oracle_lmhead(w, seed, offset, sequences=None):
+    temps = w["temperature"].cpu().numpy() if w.get("temperature") is not None else None
+    return olm.spec_verify_lmhead_single(raw(w["h_draft"]), raw(w["h_target"]), raw(w["w_vocab"]),
+                                         w["draft_tokens"].cpu().numpy(), temps, seed, offset,
+                                         sequences=sequences)
 
 
 def compare(gpu, ref, keys, sequences, bf16, report=None):

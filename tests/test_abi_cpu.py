@@ -31,7 +31,7 @@ def sv():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert set(names) == set(sv.EXPORTED)
     lib = ctypes.CDLL(sv.LIB_PATH)
     for n in names:
@@ -124,3 +124,34 @@ def test_verify_host_checks_without_gpu(sv):
     args = [ctypes.c_void_p(0x1002), ctypes.c_void_p(0x1000)] + [ctypes.c_void_p(0x1000)] * 8
     assert lib.spec_verify_single(ctypes.byref(d), *args, ctypes.c_void_p(0x10000), 1 << 20,
                                   None, None) == sv.SV_ERR_MISALIGNED
+
+
+def test_lmhead_workspace_formula_and_checks(sv):
+    """LM-head plan: flags + 20 B per sequence + draw-tile sums of fp32 rows +
+    one 16-byte partial per (GEMM row, 128-entry vocabulary tile) + merged
+    partials + gathered logits + stopped-row ids + two fp32 rows per sequence."""
+    def pad(n):
+        return (n + 255) // 256 * 256
+    B, k, V, d = 128, 4, 128256, 4096
+    M = B * (2 * k + 1)
+    nt = -(-V // 256)
+    want = (256 + pad(B * 20) + pad(B * 2 * nt * 4) + pad(M * (-(-V // 128)) * 16) +
+            pad(M * 16) + pad(M * 4) + pad(2 * B * 4) + 2 * B * V * 4)
+    assert sv.lmhead_workspace_bytes(B, k, V, d) == want
+    assert sv.lmhead_workspace_bytes(3, 2, 1001, 64) > 0
+    assert sv.lmhead_workspace_bytes(3, 2, 1001, 96) == 0          # hidden % 64 != 0
+    assert sv.lmhead_workspace_bytes(3, 2, 1001, 0) == 0
+    assert sv.lmhead_workspace_bytes(3, 2, 1001, 64, row_stride=68) == 0   # stride % 8
+    assert sv.lmhead_workspace_bytes(3, 2, 1001, 64, row_stride=72) > 0
+    lib = sv.library()
+    d32 = sv.make_desc(2, 3, 100, 0)          # fp32 is not an LM-head type
+    args = [None] * 12 + [0, None, None]
+    assert lib.spec_verify_lmhead_single(ctypes.byref(d32), 64, *args) == sv.SV_ERR_UNSUPPORTED
+    db = sv.make_desc(2, 3, 100, 1)
+    assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *args) == sv.SV_ERR_INVALID_ARG
+    assert b"NULL" in lib.spec_verify_last_error()
+    ptrs = [ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000)]
+    rest = [ctypes.c_void_p(0x1000)] * 8
+    assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *ptrs, *rest,
+                                         ctypes.c_void_p(0x10000), 1 << 30, None,
+                                         None) == sv.SV_ERR_MISALIGNED
