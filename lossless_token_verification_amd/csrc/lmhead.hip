@@ -1,7 +1,7 @@
 // LM-head path: the logits of the draft and final exits are never written to
 // memory.  A bf16 GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16) multiplies
 // the exits' hidden states by the shared head W [V, d] and reduces each
-// 128 x 128 output tile in its epilogue to the per-(row, vocabulary tile)
+// 192 x 256 output tile in its epilogue to the per-(row, vocabulary tile)
 // softmax partials the verification launch merges, plus the logit at each
 // row's drafted token.  After the decisions, the same GEMM recomputes only
 // the two rows each sequence draws from (the target row at the stop position
@@ -11,14 +11,14 @@
 // distribution (HiSpec summary, section 2 "Kernmechanismus"); with a linear
 // head the distribution is the softmax of hidden . W^T.
 //
-// Tiling (256 threads, 2 x 2 wavefronts of 64 x 64 outputs each): both
+// Tiling (512 threads, 2 x 4 wavefronts of 96 x 64 outputs each): both
 // operands are K-contiguous (hidden states [rows, d], head [V, d]), so each
 // 64-element K step of the A and W tiles is copied to LDS with 16-byte loads
-// and stores, and every MFMA operand is one 16-byte LDS read per lane.  Global
-// loads of step k+1 are issued before the MFMAs of step k (two LDS buffers,
-// one barrier per step).  Workgroup i runs on XCD i % 8; the M tiles of one
-// vocabulary tile are consecutive on one XCD, so the W tile is fetched from
-// HBM once and served to the other M tiles from that XCD's L2.
+// and stores, and every MFMA operand is one 16-byte LDS read per lane.  The
+// global loads of a step are issued two steps ahead (two register stages, two
+// LDS buffers, one barrier per step).  Workgroup i runs on XCD i % 8; the M
+// tiles of one vocabulary tile are consecutive on one XCD, so the W tile is
+// fetched from HBM once and served to the other M tiles from that XCD's L2.
 #include <algorithm>
 
 #include "sv_common.h"
@@ -30,8 +30,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WM = 2, WN = 2;          // wavefront grid of a workgroup
-constexpr int FM = 2, FN = 2;          // 32 x 32 MFMA tiles per wavefront
+constexpr int WM = kGemmWM, WN = kGemmWN;  // wavefront grid of a workgroup
+constexpr int FM = kGemmMT / (WM * 32);  // 32 x 32 MFMA tiles per wavefront, rows
+constexpr int FN = kGemmNT / (WN * 32);  // and columns
 constexpr int GT = WM * WN * kWave;    // threads per workgroup
 constexpr int MT = WM * FM * 32;
 constexpr int NT = WN * FN * 32;
@@ -41,7 +42,6 @@ constexpr int VPR = KT / 8;            // 16-byte vectors per tile row
 constexpr int A_PER = MT * VPR / GT;   // A vectors each thread copies per step
 constexpr int B_PER = NT * VPR / GT;
 static_assert(MT == kGemmMT && NT == kGemmNT, "tile sizes");
-static_assert(GT == kThreads, "one workgroup size");
 static_assert(MT * VPR % GT == 0 && NT * VPR % GT == 0, "copy slots");
 
 struct TileShared {
@@ -57,6 +57,11 @@ struct EpiShared {
   int tok[MT];      // drafted token of the row (-1: none); rows mode: source row
   float rmax[MT];
   int ridx[MT];
+};
+
+union GemmShared {
+  TileShared t;
+  EpiShared e;      // used after the last K step
 };
 
 __device__ __forceinline__ const uint16_t* a_row(const GemmArgs& a, int g) {
@@ -79,8 +84,9 @@ __device__ __forceinline__ void row_meta(const GemmArgs& a, int g, int& b, int& 
 
 template <bool ROWS>
 __global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
-  __shared__ TileShared sm;
-  __shared__ EpiShared ep;
+  __shared__ GemmShared sh;
+  TileShared& sm = sh.t;
+  EpiShared& ep = sh.e;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / WN, wn = wave - wm * WN;
   const int nM = (a.M + MT - 1) / MT;
@@ -90,39 +96,38 @@ __global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
   if (ntile >= a.n_tiles) return;   // padding of the grid to a multiple of 8 tiles
   const int m0 = mtile * MT, n0 = ntile * NT;
 
-  // copy slots of this thread: tile row v / VPR, 16-byte vector v % VPR
+  // Copy slots of this thread: tile row v / VPR, 16-byte vector v % VPR.
+  // Rows past the matrix read a valid row instead (clamped, or row 0 for a
+  // skipped recompute row): each output depends only on its own A and W rows,
+  // and the epilogue never reports those rows or columns.
   const uint16_t* ap[A_PER];
   const uint16_t* bp[B_PER];
   int aoff[A_PER], boff[B_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
     const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
-    int g = m0 + r;
-    bool ok = g < a.M;
-    if (ROWS && ok) {
-      g = a.a_rows[g];
-      ok = g >= 0;
-    }
-    ap[i] = ok ? a_row(a, g) + kv * 8 : nullptr;
+    int g = min(m0 + r, a.M - 1);
+    if (ROWS) g = max(a.a_rows[g], 0);
+    ap[i] = a_row(a, g) + kv * 8;
     aoff[i] = r * LROW + kv * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
-    const int n = n0 + r;
-    bp[i] = n < a.V ? a.w + static_cast<int64_t>(n) * a.ldw + kv * 8 : nullptr;
+    const int n = min(n0 + r, a.V - 1);
+    bp[i] = a.w + static_cast<int64_t>(n) * a.ldw + kv * 8;
     boff[i] = r * LROW + kv * 8;
   }
-  u32x4 ra[A_PER], rb[B_PER];
-  auto gload = [&](int k0) {
+  // Two register stages: the loads of step t land in stage t % 2 and are
+  // issued two steps before step t is copied to LDS.
+  u32x4 ra0[A_PER], rb0[B_PER], ra1[A_PER], rb1[B_PER];
+  auto gload = [&](int k0, u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER]) {
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      ra[i] = ap[i] ? *reinterpret_cast<const u32x4*>(ap[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < A_PER; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      rb[i] = bp[i] ? *reinterpret_cast<const u32x4*>(bp[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < B_PER; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER]) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) *reinterpret_cast<u32x4*>(&sm.a[buf][aoff[i]]) = ra[i];
 #pragma unroll
@@ -137,14 +142,12 @@ __global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[fm][fn][q] = 0.0f;
 
+  // a wavefront whose rows all lie past the matrix skips its MFMAs
+  const bool active = m0 + wm * FM * 32 < a.M;
   const int nK = a.d / KT;
   const int frow = lane & 31, fk = (lane >> 5) * 8;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nK; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nK) gload((kt + 1) * KT);
+  auto compute = [&](int cur) {
+    if (!active) return;
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
       bf16x8 af[FM], bf[FN];
@@ -164,14 +167,35 @@ __global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
     }
-    if (kt + 1 < nK) lstore(cur ^ 1);
+  };
+  // Step t: MFMAs on LDS buffer t % 2, then step t + 1 (register stage
+  // (t + 1) % 2) is copied to the other buffer and step t + 3 is loaded into
+  // that register stage.  Every load is unconditional (steps past the end
+  // reload the last one), so each copy waits only for its own stage's loads.
+  const int last = (nK - 1) * KT;
+  gload(0, ra0, rb0);
+  gload(min(KT, last), ra1, rb1);
+  lstore(0, ra0, rb0);
+  gload(min(2 * KT, last), ra0, rb0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nK; kt += 2) {
+    compute(0);
+    lstore(1, ra1, rb1);
+    gload(min((kt + 3) * KT, last), ra1, rb1);
+    __syncthreads();
+    compute(1);
+    lstore(0, ra0, rb0);
+    gload(min((kt + 4) * KT, last), ra0, rb0);
     __syncthreads();
   }
+  if (kt < nK) compute(0);   // odd number of steps: the last one is in buffer 0
 
-  // Output element (fm, fn, q) of this lane: row wm*64 + fm*32 + (q/4)*8 +
-  // h*4 + q%4, column wn*64 + fn*32 + c32 (h = lane / 32, c32 = lane % 32).
+  // Output element (fm, fn, q) of this lane: row wm*FM*32 + fm*32 + (q/4)*8 +
+  // h*4 + q%4, column wn*FN*32 + fn*32 + c32 (h = lane / 32, c32 = lane % 32).
   const int h = lane >> 5, c32 = lane & 31;
   auto row_of = [&](int fm, int q) { return wm * FM * 32 + fm * 32 + (q >> 2) * 8 + h * 4 + (q & 3); };
   auto col_of = [&](int fn) { return n0 + wn * FN * 32 + fn * 32 + c32; };

@@ -161,8 +161,10 @@ struct MergeArgs {
   int32_t n_clear;
   uint32_t* flags;
 };
-constexpr int kGemmMT = 128;   // rows per GEMM workgroup tile
-constexpr int kGemmNT = 128;   // vocabulary entries per GEMM workgroup tile
+constexpr int kGemmMT = 192;   // rows per GEMM workgroup tile
+constexpr int kGemmNT = 256;   // vocabulary entries per GEMM workgroup tile
+constexpr int kGemmWM = 2;     // wavefronts of a GEMM workgroup along rows
+constexpr int kGemmWN = 4;     // and along the vocabulary
 constexpr int kGemmKT = 64;    // hidden elements per pipeline step
 
 hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st);
