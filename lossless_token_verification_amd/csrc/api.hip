@@ -27,10 +27,11 @@ struct Plan {
   int nc = 0;
   int64_t ld = 0;
   size_t ws_bytes = 0;
-  size_t seq_bytes = 0;   // per-sequence counters and stage-1 results
+  size_t seq_bytes = 0;   // per-sequence slice counters
   size_t tile_bytes = 0;  // draw tile sums of both stages
   int nt = 0;             // draw tiles per row
-  int ns = 0;             // slices (workgroups) per sequence and stage
+  int ns = 0;             // slices (workgroups) per sequence
+  int tps = 0;            // draw tiles per slice
   int32_t exit_pos[3] = {0, 0, 0};
   int32_t exit_row0[3] = {0, 0, 0};
 };
@@ -72,9 +73,10 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   p->ld = ld;
   const int te = sv::tile_elems(d->dtype);
   p->nt = (d->vocab + te - 1) / te;
-  p->ns = (p->nt + sv::kTilesPerSlice - 1) / sv::kTilesPerSlice;
-  if (B * 2 * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
-  p->seq_bytes = (static_cast<size_t>(B) * 5 * sizeof(int32_t) + 255) / 256 * 256;
+  p->tps = num_exits == 3 ? sv::kTilesPerSliceJoint : sv::kTilesPerSlice;
+  p->ns = (p->nt + p->tps - 1) / p->tps;
+  if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
+  p->seq_bytes = (static_cast<size_t>(B) * 2 * sizeof(int32_t) + 255) / 256 * 256;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
   p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes +
                 static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
@@ -203,8 +205,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.ld = p.ld;
   sa.temperature = temperature;
   sa.partials = partials;
-  sa.clear_words = seqw;   // slice counters and completed-draw counters
-  sa.n_clear = 3 * B;
+  sa.clear_words = seqw;   // slice counters
+  sa.n_clear = 2 * B;
   sa.flags = flags;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
@@ -227,7 +229,7 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   va.window = num_exits == 3 ? window : 1;
   va.nt = p.nt;
   va.ns = p.ns;
-  va.tps = sv::kTilesPerSlice;
+  va.tps = p.tps;
   va.ld = p.ld;
   for (int e = 0; e < 3; ++e) {
     va.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
@@ -238,9 +240,6 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
     va.cnt[s] = seqw + s * B;
   }
-  va.done = seqw + 2 * B;
-  va.ytok = seqw + 3 * B;
-  va.ztok = seqw + 4 * B;
   va.tokens = tokens;
   va.temperature = temperature;
   va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
@@ -316,7 +315,7 @@ int32_t make_lm_plan(const spec_verify_desc* d, int32_t hidden, LmPlan* p) {
   p->ns = (p->nt + sv::kTilesPerSlice - 1) / sv::kTilesPerSlice;
   p->ldw = ldw;
   p->ldo = (static_cast<int64_t>(d->vocab) + 3) / 4 * 4;
-  p->seq_bytes = pad256(static_cast<size_t>(B) * 5 * sizeof(int32_t));
+  p->seq_bytes = pad256(static_cast<size_t>(B) * 2 * sizeof(int32_t));
   p->tile_bytes = pad256(static_cast<size_t>(B) * 2 * p->nt * sizeof(float));
   p->part_bytes = pad256(static_cast<size_t>(p->M) * p->n_tiles * sizeof(sv::Partial));
   p->merged_bytes = pad256(static_cast<size_t>(p->M) * sizeof(sv::Partial));
@@ -409,7 +408,7 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
     if (err != hipSuccess) return device_error(err, "event record");
   }
 
-  sv::MergeArgs ma{part, merged, g.M, p.n_tiles, seqw, 3 * B, flags};
+  sv::MergeArgs ma{part, merged, g.M, p.n_tiles, seqw, 2 * B, flags};
   err = sv::launch_merge(ma, st);
   if (err != hipSuccess) return device_error(err, "merge launch");
 
@@ -432,9 +431,6 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
     va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
     va.cnt[s] = seqw + s * B;
   }
-  va.done = seqw + 2 * B;
-  va.ytok = seqw + 3 * B;
-  va.ztok = seqw + 4 * B;
   va.tokens = tokens;
   va.temperature = temperature;
   va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);

@@ -43,12 +43,14 @@ struct Partial {
 };
 static_assert(sizeof(Partial) == 16, "Partial layout");
 
-// Workspace: [flags (256 B)] [cnt1, cnt2, done, ytok, ztok: 20 B per sequence]
+// Workspace: [flags (256 B)] [two slice counters: 8 B per sequence]
 // [tile sums: 2 * B * nt floats] [partials: rows * nc], each area padded to
 // 256 B.
 constexpr size_t kFlagsBytes = 256;
-// Draw tiles each workgroup of a verification stage sums.
+// Draw tiles each workgroup of a verification sums: two rows per tile for a
+// single draw, three for the hierarchy's joint draw of y and z.
 constexpr int kTilesPerSlice = 128;
+constexpr int kTilesPerSliceJoint = 64;
 
 // Row statistics of every logit row (the HBM stream).
 struct StatsArgs {
@@ -74,10 +76,8 @@ struct VerifyArgs {
   int32_t exit_row0[3];
   const Partial* partials;
   float* tsum[2];          // [B, nt] tile sums of each stage's draw
-  int32_t* cnt[2];         // [B] slices done per stage
-  int32_t* done;           // [B] draws of the sequence completed
-  int32_t* ytok;           // [B] stage-1 token y
-  int32_t* ztok;           // [B] stage-2 correction drawn beside y
+  int32_t* cnt[2];         // [B] slices done: cnt[0] joint or single draw, cnt[1] the
+                           // hierarchy's stage-2 draw before a1
   const int32_t* tokens;
   const float* temperature;
   uint32_t key0, key1, offset;

@@ -1,6 +1,6 @@
 // Per-sequence verification (one verification stage, all sequences).
 //
-// A stage runs as B * ns workgroups, ns slices of the vocabulary per sequence.
+// A launch runs as B * ns workgroups, ns slices of the vocabulary per sequence.
 // Every workgroup of a sequence first takes the stage's decision itself (the
 // same bits in every slice):
 //   1. merge the chunk partials of the sequence's rows into (reference c,
@@ -10,9 +10,10 @@
 //      block for (j, b, stage, offset), accept iff u * q(x) < p(x); a ballot
 //      gives the first rejection (windows of the given size examined in order).
 // Then each workgroup sums the draw weights -- max(0, p - q) for a correction,
-// p for the bonus -- over its slice of 16 tiles (one 16-byte load per lane and
-// row per tile), and the last workgroup of the sequence locates the token: an
-// fp64 scan of the tile sums, then one wavefront rescans the chosen tile.
+// p for the bonus -- over its slice of tiles (one 16-byte load per lane and
+// row per tile; 128 tiles per slice, 64 for the hierarchy's joint draw of y
+// and z), and the last workgroup of the sequence locates the token: an fp64
+// scan of the tile sums, then one wavefront rescans the chosen tile.
 //
 // Stage 1 (or the single stage) compares the draft exit with the target exit;
 // stage 2 of the hierarchy compares L_i with L_f on the tentative tokens (HiSpec
@@ -198,6 +199,94 @@ __device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, c
     if (t >= t_end) break;
     fa = fetch(t + stride, ap, aq);
     reduce(t, fb, bp, bq);
+    t += stride;
+  }
+}
+
+// The hierarchy's two draws at one position in one pass: over tiles
+// [t_begin, t_end), the weights of y (p = L_i, q = L_d, or L_i alone for the
+// bonus) and of z (p = L_f, q = L_i) are summed per tile from one read of each
+// of the three rows and stored (device-scope) to out_y[t] and out_z[t].
+template <int DT>
+__device__ __forceinline__ void tile_pass_joint(const char* irow, const RowStat& ist,
+                                                const char* drow, const RowStat& dst, bool has_d,
+                                                const char* frow, const RowStat& fst, float s,
+                                                int V, int t_begin, int t_end, float* out_y,
+                                                float* out_z) {
+  constexpr int VPE = RowT<DT>::VPE;
+  constexpr int ES = RowT<DT>::ES;
+  constexpr int TE = kWave * VPE;
+  constexpr int G = 2;
+  constexpr int stride = kWaves * G;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(irow) | reinterpret_cast<uintptr_t>(frow) |
+                        (has_d ? reinterpret_cast<uintptr_t>(drow) : 0)) & 15) == 0;
+  const float ci = ist.key, isi = ist.inv_S, cf = fst.key, isf = fst.inv_S;
+  const float cd = has_d ? dst.key : 0.0f, isd = has_d ? dst.inv_S : 0.0f;
+
+  auto fetch = [&](int t0, u32x4 (&vi)[G], u32x4 (&vd)[G], u32x4 (&vf)[G]) -> bool {
+    if (!(t0 < t_end && vec_ok && (t0 + G) * TE <= V)) return false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t off = static_cast<int64_t>((t0 + g) * TE + lane * VPE) * ES;
+      vi[g] = *reinterpret_cast<const u32x4*>(irow + off);
+      vf[g] = *reinterpret_cast<const u32x4*>(frow + off);
+      if (has_d) vd[g] = *reinterpret_cast<const u32x4*>(drow + off);
+    }
+    return true;
+  };
+  auto sums = [&](const float (&xi)[VPE], float (&xd)[VPE], const float (&xf)[VPE], float& sy,
+                  float& sz) {
+    if (!has_d)
+#pragma unroll
+      for (int q = 0; q < VPE; ++q) xd[q] = 0.0f;
+    sy = wave_sum(lane_weight_sum<DT>(xi, xd, s, ci, isi, cd, isd, has_d));
+    sz = wave_sum(lane_weight_sum<DT>(xf, xi, s, cf, isf, ci, isi, true));
+  };
+  auto reduce = [&](int t0, bool fetched, const u32x4 (&vi)[G], const u32x4 (&vd)[G],
+                    const u32x4 (&vf)[G]) {
+    float sy[G], sz[G];
+    if (fetched) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float xi[VPE], xd[VPE], xf[VPE];
+        unpack_vec<DT>(vi[g], xi);
+        unpack_vec<DT>(vf[g], xf);
+        if (has_d) unpack_vec<DT>(vd[g], xd);
+        sums(xi, xd, xf, sy[g], sz[g]);
+      }
+    } else {
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        float xi[VPE], xd[VPE], xf[VPE];
+        const int e = (t0 + g) * TE + lane * VPE;
+        load_group<DT>(irow, e, V, vec_ok, xi);
+        load_group<DT>(frow, e, V, vec_ok, xf);
+        if (has_d) load_group<DT>(drow, e, V, vec_ok, xd);
+        sums(xi, xd, xf, sy[g], sz[g]);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (t0 + g < t_end) {
+          store_coherent(out_y + t0 + g, sy[g]);
+          store_coherent(out_z + t0 + g, sz[g]);
+        }
+      }
+    }
+  };
+
+  int t = t_begin + wave * G;
+  u32x4 ai[G], ad[G], af[G], bi[G], bd[G], bf[G];
+  bool fa = fetch(t, ai, ad, af);
+  while (t < t_end) {
+    const bool fb = fetch(t + stride, bi, bd, bf);
+    reduce(t, fa, ai, ad, af);
+    t += stride;
+    if (t >= t_end) break;
+    fa = fetch(t + stride, ai, ad, af);
+    reduce(t, fb, bi, bd, bf);
     t += stride;
   }
 }
@@ -706,23 +795,28 @@ __device__ __forceinline__ void load_drafts(SeqCtx<DT>& cx, int n) {
   if (t >= 0 && t < n) cx.sm.toks[t] = cx.a.tokens[static_cast<int64_t>(cx.b) * cx.k + t];
 }
 
+// Counts slice g of a sequence done after its tile sums were published; true
+// in the workgroup that completes the draw.  Uniform across the workgroup.
+__device__ __forceinline__ bool slice_done(int32_t* cnt, int ns, VerifyShared& sm) {
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) sm.sh[1] = (atomicAdd(cnt, 1) == ns - 1);
+  __syncthreads();
+  const bool last = sm.sh[1] != 0;
+  __syncthreads();
+  return last;
+}
+
 // Sums slice g of a draw's tiles (p rows at pr, q rows at qr when has_q) and
 // counts it done; true in the workgroup that completes the draw.
 template <int DT>
 __device__ bool draw_slice(SeqCtx<DT>& cx, int g, int stage, const char* pr, const char* qr,
                            bool has_q, const RowStat& ps, const RowStat& qs) {
   const VerifyArgs& a = cx.a;
-  VerifyShared& sm = cx.sm;
   float* tsum = a.tsum[stage] + static_cast<int64_t>(cx.b) * a.nt;
   const int t0 = g * a.tps;
   tile_pass<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, t0, min(a.nt, t0 + a.tps), tsum, true);
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) sm.sh[1] = (atomicAdd(a.cnt[stage] + cx.b, 1) == a.ns - 1);
-  __syncthreads();
-  const bool last = sm.sh[1] != 0;
-  __syncthreads();
-  return last;
+  return slice_done(a.cnt[stage] + cx.b, a.ns, cx.sm);
 }
 
 // In the workgroup that completed a draw: locate the token from the tile sums
@@ -759,22 +853,20 @@ __device__ int sliced_draw(SeqCtx<DT>& cx, int slice, int qe, int pe, int apos, 
   return draw_finish<DT>(cx, stage, pr, qr, has_q, ps, qs, v);
 }
 
-// One launch, grid B * ns (single stage) or B * 2ns (hierarchy): workgroup w
-// of sequence b works on draw w / ns, slice w % ns.  Every workgroup takes
-// stage 1's decision itself (and, for the hierarchy, stage 2's decision on the
-// drafted tokens before a1, which does not depend on the L_i token y).  Then
-// the draws the sequence needs run side by side:
-//  - stage 2 rejected drafted token a2p < a1: y is never emitted; draw 0 is
-//    stage 2's correction at a2p, and the sequence is done;
-//  - otherwise draw 0 is y (stage 1's correction, or its bonus), and for the
-//    hierarchy draw 1 is stage 2's correction at a1 -- which depends only on
-//    the rows L_f[a1], L_i[a1] and its own uniform, not on y.  The workgroup
-//    completing the second of the two tests y against L_f: emitting t when
-//    L_f accepts it, else t[:a1] and the correction.
+// One launch, grid B * ns: workgroup w of sequence b works on vocabulary slice
+// w.  Every workgroup takes stage 1's decision itself (and, for the hierarchy,
+// stage 2's decision on the drafted tokens before a1, which does not depend on
+// the L_i token y).  Then:
+//  - single stage: the correction or bonus draw;
+//  - hierarchy, stage 2 rejects drafted token a2p < a1: y is never emitted;
+//    stage 2's correction at a2p is drawn;
+//  - hierarchy otherwise: y (stage 1's correction, or its bonus) and stage 2's
+//    correction z at a1 are summed in one pass over L_d[a1], L_i[a1], L_f[a1];
+//    the workgroup completing the last slice locates y, tests it against L_f,
+//    and locates z only if L_f rejects y.
 template <int DT>
-__device__ void verify_slice(const VerifyArgs& a, int b, int w, VerifyShared& sm) {
-  const int draw = w / a.ns, slice = w - draw * a.ns;
-  const bool first = w == 0;
+__device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared& sm) {
+  const bool first = slice == 0;
   SeqCtx<DT> cx(a, sm, b, first);
   const int tid = threadIdx.x, k = a.k;
   const int diag_pos = k + 1;
@@ -816,17 +908,18 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int w, VerifyShared& sm
     if (cx.greedy) cx.write_outputs(a1 + 1, sm.st[1][a1].amax, a1, -1);
     return;
   }
+  const bool early = a.hier && a2p < a1;   // stage 2 rejects drafted token a2p
   if (first && a.diag_draws && tid < 8) {
-    // draw diagnostics of the draws that do not happen (the others are written
-    // by the workgroup completing each draw)
+    // draws that do not happen (the workgroup completing each draw writes the
+    // others; the hierarchy's stage-2 entry is always written there)
     const int stage = tid / 4;
-    const bool drawn = !cx.greedy && (stage == 0 ? !(a.hier && a2p < a1) : a.hier);
+    const bool drawn = !cx.greedy && (stage == 0 ? !early : a.hier);
     if (!drawn) a.diag_draws[static_cast<int64_t>(b) * 8 + tid] = NAN;
   }
 
   if (cx.greedy) {   // argmax tokens: no draw, the first workgroup finishes
     if (!first) return;
-    if (a.hier && a2p < a1) {
+    if (early) {
       cx.write_outputs(a2p + 1, sm.st[2][a2p].amax, a1, a2p);
       return;
     }
@@ -841,60 +934,50 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int w, VerifyShared& sm
     return;
   }
 
-  // which draw this workgroup works on (one call site keeps one copy of it)
-  const bool early = a.hier && a2p < a1;   // stage 2 rejects drafted token a2p
-  if (early && draw != 0) return;
-  int stage, apos;
-  bool has_q;
-  float v;
-  if (early) {            // stage 2's correction at a2p; y is never emitted
-    stage = 1;
-    apos = a2p;
-    has_q = true;
-    v = sm.vs2[a2p];
-  } else if (draw == 0) { // y: stage 1's correction or bonus
-    stage = 0;
-    apos = a1;
-    has_q = a1 < k;
-    v = v1;
-  } else {                // stage 2's correction at a1, used if L_f rejects y
-    stage = 1;
-    apos = a1;
-    has_q = true;
-    v = sm.vs2[a1];
+  if (a.hier && !early) {
+    const bool has_q = a1 < k;
+    const char* li = cx.row_ptr(1, a1);
+    const char* ld = has_q ? cx.row_ptr(0, a1) : nullptr;
+    const char* lf = cx.row_ptr(2, a1);
+    float* ty = a.tsum[0] + static_cast<int64_t>(b) * a.nt;
+    float* tz = a.tsum[1] + static_cast<int64_t>(b) * a.nt;
+    const int t0 = slice * a.tps;
+    const RowStat& si = sm.st[1][a1];
+    const RowStat& sd = sm.st[0][has_q ? a1 : 0];
+    const RowStat& sf = sm.st[2][a1];
+    tile_pass_joint<DT>(li, si, ld, sd, has_q, lf, sf, cx.s, cx.V, t0, min(a.nt, t0 + a.tps),
+                        ty, tz);
+    if (!slice_done(a.cnt[0] + b, a.ns, sm)) return;
+    DrawResult ry = locate<DT>(li, si, ld, sd, has_q, cx.s, cx.V, v1, a.nt, ty, true, sm);
+    if (ry.y < 0) ry = draw_tokens<DT>(li, si, nullptr, si, false, cx.s, cx.V, v1, sm);
+    cx.write_draw_diag(0, ry);
+    const int y = ry.y;
+    if (tid == 0) sm.toks[a1] = y;
+    if (cx.accept_y(a1, y, true)) {
+      DrawResult none;
+      nan_draw(none);
+      cx.write_draw_diag(1, none);
+      cx.write_outputs(a1 + 1, y, a1, a1 + 1);
+      return;
+    }
+    const float v2 = sm.vs2[a1];
+    DrawResult rz = locate<DT>(lf, sf, li, si, true, cx.s, cx.V, v2, a.nt, tz, true, sm);
+    if (rz.y < 0) rz = draw_tokens<DT>(lf, sf, nullptr, sf, false, cx.s, cx.V, v2, sm);
+    cx.write_draw_diag(1, rz);
+    cx.write_outputs(a1 + 1, rz.y, a1, a1);
+    return;
   }
+
+  // single stage, or the hierarchy's stage-2 correction at a2p < a1
+  const int stage = early ? 1 : 0;
+  const int apos = early ? a2p : a1;
+  const bool has_q = early || a1 < k;
+  const float v = early ? sm.vs2[a2p] : v1;
   const int tok = sliced_draw<DT>(cx, slice, stage, stage + 1, apos, has_q, stage, v,
                                   sm.st[stage + 1][apos], sm.st[stage][has_q ? apos : 0]);
   if (tok == -2) return;
-  if (early) {
-    cx.write_outputs(a2p + 1, tok, a1, a2p);
-    return;
-  }
-  if (!a.hier) {
-    cx.write_outputs(a1 + 1, tok, a1, -1);
-    return;
-  }
-  // this workgroup completed one of the two draws: the one completing the
-  // second finishes the sequence
-  if (tid == 0) {
-    store_coherent(draw == 0 ? a.ytok + b : a.ztok + b, tok);
-    wait_memory();
-    sm.sh[7] = atomicAdd(a.done + b, 1);
-  }
-  __syncthreads();
-  if (sm.sh[7] != 1) return;
-  if (tid == 0) {
-    sm.sh[5] = load_coherent(a.ytok + b);
-    sm.sh[6] = load_coherent(a.ztok + b);
-  }
-  __syncthreads();
-  const int y = sm.sh[5], z = sm.sh[6];
-  if (tid == 0) sm.toks[a1] = y;
-  if (cx.accept_y(a1, y, true)) {
-    cx.write_outputs(a1 + 1, y, a1, a1 + 1);
-  } else {
-    cx.write_outputs(a1 + 1, z, a1, a1);
-  }
+  if (early) cx.write_outputs(a2p + 1, tok, a1, a2p);
+  else cx.write_outputs(a1 + 1, tok, a1, -1);
 }
 
 }  // namespace sv

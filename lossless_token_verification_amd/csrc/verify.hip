@@ -11,9 +11,8 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void verify_kernel(VerifyArgs a) {
   __shared__ VerifyShared sm;
-  const int per_seq = a.hier ? 2 * a.ns : a.ns;
-  const int b = blockIdx.x / per_seq;
-  verify_slice<DT>(a, b, blockIdx.x - b * per_seq, sm);
+  const int b = blockIdx.x / a.ns;
+  verify_slice<DT>(a, b, blockIdx.x - b * a.ns, sm);
 }
 
 // Packed (unpadded) tokens: cu_offsets by a single-workgroup scan of the
@@ -51,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
 }  // namespace
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.hier ? 2 * a.ns : a.ns));
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.ns));
   if (a.dtype == 1)
     hipLaunchKernelGGL(verify_kernel<1>, grid, dim3(kThreads), 0, st, a);
   else

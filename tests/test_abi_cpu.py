@@ -48,7 +48,7 @@ def test_version_and_status_strings(sv):
 
 
 def test_workspace_size_formula(sv):
-    # 256 B of flags + 20 B per sequence + 2 draw-tile sums per (sequence, tile)
+    # 256 B of flags + 8 B per sequence + 2 draw-tile sums per (sequence, tile)
     # (each area padded to 256 B) + one 16-byte partial per (row, 64 KiB chunk)
     def pad(n):
         return (n + 255) // 256 * 256
@@ -56,11 +56,11 @@ def test_workspace_size_formula(sv):
     def tiles(V, per):
         return -(-V // per)
     assert sv.workspace_bytes(256, 8, 128256, 1, 3) == \
-        256 + pad(256 * 20) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
+        256 + pad(256 * 8) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
     assert sv.workspace_bytes(64, 4, 32000, 1, 2) == \
-        256 + pad(64 * 20) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
+        256 + pad(64 * 8) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
     assert sv.workspace_bytes(32, 5, 151936, 0, 2) == \
-        256 + pad(32 * 20) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
+        256 + pad(32 * 8) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 
@@ -127,7 +127,7 @@ def test_verify_host_checks_without_gpu(sv):
 
 
 def test_lmhead_workspace_formula_and_checks(sv):
-    """LM-head plan: flags + 20 B per sequence + draw-tile sums of fp32 rows +
+    """LM-head plan: flags + 8 B per sequence + draw-tile sums of fp32 rows +
     one 16-byte partial per (GEMM row, 256-entry vocabulary tile) + merged
     partials + gathered logits + stopped-row ids + two fp32 rows per sequence."""
     def pad(n):
@@ -135,7 +135,7 @@ def test_lmhead_workspace_formula_and_checks(sv):
     B, k, V, d = 128, 4, 128256, 4096
     M = B * (2 * k + 1)
     nt = -(-V // 256)
-    want = (256 + pad(B * 20) + pad(B * 2 * nt * 4) + pad(M * (-(-V // 256)) * 16) +
+    want = (256 + pad(B * 8) + pad(B * 2 * nt * 4) + pad(M * (-(-V // 256)) * 16) +
             pad(M * 16) + pad(M * 4) + pad(2 * B * 4) + 2 * B * V * 4)
     assert sv.lmhead_workspace_bytes(B, k, V, d) == want
     assert sv.lmhead_workspace_bytes(3, 2, 1001, 64) > 0
