@@ -63,6 +63,26 @@ struct RowT {
   static constexpr int ES = DT == 1 ? 2 : 4;
 };
 
+// Sum over the wavefront of one float per lane, returned to every lane.  DPP
+// moves (VALU only, no LDS round trip): an inclusive scan within each row of 16
+// lanes (row_shr 1, 2, 4, 8), then row 1 and 3 add the last lane of the row
+// before (row_bcast 15) and rows 2 and 3 that of row 1 (row_bcast 31); lane
+// 63 then holds the total.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf,
+                                                         false));
+}
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);   // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);   // row_bcast:15
+  v = dpp_add<0x143, 0xc>(v);   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));   // the bits, not a cast
+}
+
 // Draw weight of one element: p(v) or max(0, p(v) - q(v)), in fp32.
 // Contraction is off so every evaluation of the same element gives the same
 // bits (the tile pass and the rescan must agree).
@@ -171,7 +191,7 @@ __device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, c
         else
 #pragma unroll
           for (int q = 0; q < VPE; ++q) xq[q] = 0.0f;
-        sums[g] = wave_sum(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
+        sums[g] = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
       }
     } else {
 #pragma unroll 1
@@ -183,7 +203,7 @@ __device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, c
         else
 #pragma unroll
           for (int q = 0; q < VPE; ++q) xq[q] = 0.0f;
-        sums[g] = wave_sum(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
+        sums[g] = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
       }
     }
     emit(t0, sums);
@@ -240,8 +260,8 @@ __device__ __forceinline__ void tile_pass_joint(const char* irow, const RowStat&
     if (!has_d)
 #pragma unroll
       for (int q = 0; q < VPE; ++q) xd[q] = 0.0f;
-    sy = wave_sum(lane_weight_sum<DT>(xi, xd, s, ci, isi, cd, isd, has_d));
-    sz = wave_sum(lane_weight_sum<DT>(xf, xi, s, cf, isf, ci, isi, true));
+    sy = wave_total(lane_weight_sum<DT>(xi, xd, s, ci, isi, cd, isd, has_d));
+    sz = wave_total(lane_weight_sum<DT>(xf, xi, s, cf, isf, ci, isi, true));
   };
   auto reduce = [&](int t0, bool fetched, const u32x4 (&vi)[G], const u32x4 (&vd)[G],
                     const u32x4 (&vf)[G]) {
