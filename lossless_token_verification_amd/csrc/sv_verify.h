@@ -53,6 +53,7 @@ struct VerifyShared {
   float vs1[kMaxPositions];  // stage-1 draw uniforms (hierarchy)
   float vs2[kMaxPositions];  // stage-2 draw uniforms (hierarchy)
   float us2[kMaxPositions];  // stage-2 accept uniforms (hierarchy)
+  DrawResult pr[2];          // draws located side by side by two wavefronts
   int sh[8];
 };
 static_assert(sizeof(float) * kMaxTiles >= 1024 * sizeof(Partial), "partial staging");
@@ -314,137 +315,143 @@ __device__ __forceinline__ void tile_pass_joint(const char* irow, const RowStat&
 // Inverse CDF over NT tile sums (from LDS, or coherent loads from global when
 // `coherent`): y = the smallest index with C(y) > v * R, or, when rounding
 // leaves none, the largest index with a positive weight; y = -1 when R == 0.
-// Wavefront 0 does the work (lane l owns a contiguous run of tiles: fp64 lane
-// sums, a wavefront scan, then a rescan of the chosen tile); all threads must
-// call it (it ends with a barrier and returns the result to every thread).
+// One wavefront does the work (lane l owns a contiguous run of tiles: fp64
+// lane sums, a wavefront scan, then a rescan of the chosen tile); the result
+// is the same in every lane of that wavefront.
+template <int DT>
+__device__ __forceinline__ DrawResult locate_wave(const char* prow, const RowStat& ps,
+                                                  const char* qrow, const RowStat& qs, bool has_q,
+                                                  float s, int V, float v, int NT,
+                                                  const float* tiles, bool coherent) {
+  constexpr int VPE = RowT<DT>::VPE;
+  constexpr int TE = kWave * VPE;
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) |
+                        (has_q ? reinterpret_cast<uintptr_t>(qrow) : 0)) & 15) == 0;
+  const float cp = ps.key, isp = ps.inv_S;
+  const float cq = has_q ? qs.key : 0.0f, isq = has_q ? qs.inv_S : 0.0f;
+  auto tile_at = [&](int i) -> float { return coherent ? load_coherent(tiles + i) : tiles[i]; };
+  const int per = (NT + kWave - 1) / kWave;
+  const int lo = min(NT, lane * per), hi = min(NT, lo + per);
+  double mine = 0.0;
+  for (int i = lo; i < hi; ++i) mine += static_cast<double>(tile_at(i));
+  double incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double up = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += up;
+  }
+  const double R = __shfl(incl, kWave - 1, kWave);
+  const double up1 = __shfl_up(incl, 1, kWave);
+  const double excl = lane > 0 ? up1 : 0.0;
+  const double tv = static_cast<double>(v) * R;
+  int y = -1;
+  double c_lo = 0.0, c_hi = 0.0;
+  if (R > 0.0) {
+    // The chosen token has a positive weight, so only tiles with a positive
+    // sum can hold it (this also absorbs rounding between the lanes' runs).
+    int cross_t = -1, last_t = -1;
+    double cross_base = 0.0, last_base = 0.0, run = excl;
+    for (int i = lo; i < hi; ++i) {
+      const float ti = tile_at(i);
+      const double nxt = run + static_cast<double>(ti);
+      if (ti > 0.0f) {
+        if (cross_t < 0 && nxt > tv) {
+          cross_t = i;
+          cross_base = run;
+        }
+        last_t = i;
+        last_base = run;
+      }
+      run = nxt;
+    }
+    const unsigned long long cmask = __ballot(cross_t >= 0);
+    const bool overrun = cmask == 0;
+    int TT;
+    double base;
+    if (!overrun) {
+      const int src = __ffsll(cmask) - 1;
+      TT = __shfl(cross_t, src, kWave);
+      base = __shfl(cross_base, src, kWave);
+    } else {
+      const unsigned long long lmask = __ballot(last_t >= 0);
+      const int src = 63 - __clzll(lmask);
+      TT = __shfl(last_t, src, kWave);
+      base = __shfl(last_base, src, kWave);
+    }
+    // rescan tile TT element by element in fp64
+    const int e = TT * TE + lane * VPE;
+    float xp[VPE], xq[VPE], w[VPE];
+    load_group<DT>(prow, e, V, vec_ok, xp);
+    if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
+    double lsum = 0.0;
+#pragma unroll
+    for (int q = 0; q < VPE; ++q) {
+      w[q] = weight(xp[q], has_q ? xq[q] : 0.0f, s, cp, isp, cq, isq, has_q);
+      lsum += static_cast<double>(w[q]);
+    }
+    double li = lsum;   // inclusive prefix of lane sums
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double up = __shfl_up(li, o, kWave);
+      if (lane >= o) li += up;
+    }
+    const double lup = __shfl_up(li, 1, kWave);
+    double r2 = base + (lane > 0 ? lup : 0.0);
+    int cross = -1, lastpos = -1;
+    double x_lo = 0.0, x_hi = 0.0, l_lo = 0.0, l_hi = 0.0;
+#pragma unroll
+    for (int q = 0; q < VPE; ++q) {
+      const double nxt = r2 + static_cast<double>(w[q]);
+      if (w[q] > 0.0f) {
+        if (!overrun && cross < 0 && nxt > tv) {
+          cross = q;
+          x_lo = r2;
+          x_hi = nxt;
+        }
+        lastpos = q;
+        l_lo = r2;
+        l_hi = nxt;
+      }
+      r2 = nxt;
+    }
+    const unsigned long long xm = __ballot(cross >= 0);
+    if (xm) {
+      const int src = __ffsll(xm) - 1;
+      y = TT * TE + src * VPE + __shfl(cross, src, kWave);
+      c_lo = __shfl(x_lo, src, kWave);
+      c_hi = __shfl(x_hi, src, kWave);
+    } else {
+      // no crossing: the last element of the tile with a positive weight
+      const unsigned long long pm = __ballot(lastpos >= 0);
+      const int src = pm ? 63 - __clzll(pm) : 0;
+      const int yq = __shfl(lastpos, src, kWave);
+      c_lo = __shfl(l_lo, src, kWave);
+      c_hi = __shfl(l_hi, src, kWave);
+      y = pm ? TT * TE + src * VPE + yq : -1;
+    }
+  }
+  DrawResult res;
+  res.y = y;
+  res.R = R;
+  res.t = tv;
+  res.c_lo = c_lo;
+  res.c_hi = c_hi;
+  return res;
+}
+
+// locate_wave on wavefront 0, result returned to every thread (all threads
+// call it; it contains barriers).
 template <int DT>
 __device__ __forceinline__ DrawResult locate(const char* prow, const RowStat& ps, const char* qrow,
                              const RowStat& qs, bool has_q, float s, int V, float v, int NT,
                              const float* tiles, bool coherent, VerifyShared& sm) {
-  constexpr int VPE = RowT<DT>::VPE;
-  constexpr int TE = kWave * VPE;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  if (tid < kWave) {
-    const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) |
-                          (has_q ? reinterpret_cast<uintptr_t>(qrow) : 0)) & 15) == 0;
-    const float cp = ps.key, isp = ps.inv_S;
-    const float cq = has_q ? qs.key : 0.0f, isq = has_q ? qs.inv_S : 0.0f;
-    auto tile_at = [&](int i) -> float { return coherent ? load_coherent(tiles + i) : tiles[i]; };
-    const int per = (NT + kWave - 1) / kWave;
-    const int lo = min(NT, lane * per), hi = min(NT, lo + per);
-    double mine = 0.0;
-    for (int i = lo; i < hi; ++i) mine += static_cast<double>(tile_at(i));
-    double incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double up = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += up;
-    }
-    const double R = __shfl(incl, kWave - 1, kWave);
-    const double up1 = __shfl_up(incl, 1, kWave);
-    const double excl = lane > 0 ? up1 : 0.0;
-    const double tv = static_cast<double>(v) * R;
-    int y = -1;
-    double c_lo = 0.0, c_hi = 0.0;
-    if (R > 0.0) {
-      // The chosen token has a positive weight, so only tiles with a positive
-      // sum can hold it (this also absorbs rounding between the lanes' runs).
-      int cross_t = -1, last_t = -1;
-      double cross_base = 0.0, last_base = 0.0, run = excl;
-      for (int i = lo; i < hi; ++i) {
-        const float ti = tile_at(i);
-        const double nxt = run + static_cast<double>(ti);
-        if (ti > 0.0f) {
-          if (cross_t < 0 && nxt > tv) {
-            cross_t = i;
-            cross_base = run;
-          }
-          last_t = i;
-          last_base = run;
-        }
-        run = nxt;
-      }
-      const unsigned long long cmask = __ballot(cross_t >= 0);
-      const bool overrun = cmask == 0;
-      int TT;
-      double base;
-      if (!overrun) {
-        const int src = __ffsll(cmask) - 1;
-        TT = __shfl(cross_t, src, kWave);
-        base = __shfl(cross_base, src, kWave);
-      } else {
-        const unsigned long long lmask = __ballot(last_t >= 0);
-        const int src = 63 - __clzll(lmask);
-        TT = __shfl(last_t, src, kWave);
-        base = __shfl(last_base, src, kWave);
-      }
-      // rescan tile TT element by element in fp64
-      const int e = TT * TE + lane * VPE;
-      float xp[VPE], xq[VPE], w[VPE];
-      load_group<DT>(prow, e, V, vec_ok, xp);
-      if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
-      double lsum = 0.0;
-#pragma unroll
-      for (int q = 0; q < VPE; ++q) {
-        w[q] = weight(xp[q], has_q ? xq[q] : 0.0f, s, cp, isp, cq, isq, has_q);
-        lsum += static_cast<double>(w[q]);
-      }
-      double li = lsum;   // inclusive prefix of lane sums
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double up = __shfl_up(li, o, kWave);
-        if (lane >= o) li += up;
-      }
-      const double lup = __shfl_up(li, 1, kWave);
-      double r2 = base + (lane > 0 ? lup : 0.0);
-      int cross = -1, lastpos = -1;
-      double x_lo = 0.0, x_hi = 0.0, l_lo = 0.0, l_hi = 0.0;
-#pragma unroll
-      for (int q = 0; q < VPE; ++q) {
-        const double nxt = r2 + static_cast<double>(w[q]);
-        if (w[q] > 0.0f) {
-          if (!overrun && cross < 0 && nxt > tv) {
-            cross = q;
-            x_lo = r2;
-            x_hi = nxt;
-          }
-          lastpos = q;
-          l_lo = r2;
-          l_hi = nxt;
-        }
-        r2 = nxt;
-      }
-      const unsigned long long xm = __ballot(cross >= 0);
-      if (xm) {
-        const int src = __ffsll(xm) - 1;
-        y = TT * TE + src * VPE + __shfl(cross, src, kWave);
-        c_lo = __shfl(x_lo, src, kWave);
-        c_hi = __shfl(x_hi, src, kWave);
-      } else {
-        // no crossing: the last element of the tile with a positive weight
-        const unsigned long long pm = __ballot(lastpos >= 0);
-        const int src = pm ? 63 - __clzll(pm) : 0;
-        const int yq = __shfl(lastpos, src, kWave);
-        c_lo = __shfl(l_lo, src, kWave);
-        c_hi = __shfl(l_hi, src, kWave);
-        y = pm ? TT * TE + src * VPE + yq : -1;
-      }
-    }
-    if (lane == 0) {
-      sm.iscr[2] = y;
-      sm.dscr[0] = R;
-      sm.dscr[1] = tv;
-      sm.dscr[2] = c_lo;
-      sm.dscr[3] = c_hi;
-    }
+  if (threadIdx.x < kWave) {
+    const DrawResult r = locate_wave<DT>(prow, ps, qrow, qs, has_q, s, V, v, NT, tiles, coherent);
+    if (threadIdx.x == 0) sm.pr[0] = r;
   }
   __syncthreads();
-  DrawResult res;
-  res.y = sm.iscr[2];
-  res.R = sm.dscr[0];
-  res.t = sm.dscr[1];
-  res.c_lo = sm.dscr[2];
-  res.c_hi = sm.dscr[3];
+  const DrawResult res = sm.pr[0];
   __syncthreads();   // scratch may be reused by the caller
   return res;
 }
@@ -511,6 +518,25 @@ struct SeqCtx {
     s = greedy ? 0.0f : kLog2e / tau;
     if (report && bad_tau && threadIdx.x == 0) atomicOr(a.flags, kFlagTemperature);
   }
+
+  // Logits of each drafted token in the rows at its position (wavefront 0,
+  // lane j < k), loaded before the statistics merge so that the two memory
+  // latencies overlap; the LM-head path reads them from `gath`.
+  float g[3] = {0.0f, 0.0f, 0.0f};
+
+  __device__ void pregather(int nexits) {
+    const int j = threadIdx.x;
+    if (j >= k || greedy) return;
+    const int x = a.tokens[static_cast<int64_t>(b) * k + j];
+    if (x < 0 || x >= V) return;
+    auto at = [&](int e) {
+      return a.gath ? a.gath[row_index(e, j)] : load_elem(row_ptr(e, j), x, DT);
+    };
+    g[0] = at(0);
+    g[1] = at(1);
+    if (nexits > 2) g[2] = at(2);
+  }
+  __device__ float gathered(int e) const { return e == 0 ? g[0] : (e == 1 ? g[1] : g[2]); }
 
   __device__ int positions(int e) const { return e == 0 ? k : k + 1; }
 
@@ -603,9 +629,9 @@ struct SeqCtx {
           q1 = valid && x == sm.st[0][j].amax ? 1.0 : 0.0;
           p2 = mf ? 1.0 : 0.0;
         } else if (valid) {
-          const float ld = load_elem(row_ptr(0, j), x, DT);
-          const float li = load_elem(row_ptr(1, j), x, DT);
-          const float lf = load_elem(row_ptr(2, j), x, DT);
+          const float ld = g[0];
+          const float li = g[1];
+          const float lf = g[2];
           q1 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(ld, s, -sm.st[0][j].key))) /
                sm.st[0][j].S;
           p1 = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(li, s, -sm.st[1][j].key))) /
@@ -730,8 +756,8 @@ struct SeqCtx {
           pj = valid && x == sm.st[pe][j].amax ? 1.0 : 0.0;
           qj = valid && x == sm.st[qe][j].amax ? 1.0 : 0.0;
         } else if (valid) {
-          const float lp = a.gath ? a.gath[row_index(pe, j)] : load_elem(row_ptr(pe, j), x, DT);
-          const float lq = a.gath ? a.gath[row_index(qe, j)] : load_elem(row_ptr(qe, j), x, DT);
+          const float lp = gathered(pe);
+          const float lq = gathered(qe);
           const float ep = __builtin_amdgcn_exp2f(fmaf(lp, s, -sm.st[pe][j].key));
           const float eq = __builtin_amdgcn_exp2f(fmaf(lq, s, -sm.st[qe][j].key));
           pj = static_cast<double>(ep) / sm.st[pe][j].S;
@@ -903,6 +929,7 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
       d[0] = d[1] = NAN;
     }
   }
+  cx.pregather(a.hier ? 3 : 2);
   cx.merge_all(k, k + 1, a.hier ? k + 1 : 0);
   int a1, a2p;
   float v1;
@@ -968,7 +995,18 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
     tile_pass_joint<DT>(li, si, ld, sd, has_q, lf, sf, cx.s, cx.V, t0, min(a.nt, t0 + a.tps),
                         ty, tz);
     if (!slice_done(a.cnt[0] + b, a.ns, sm)) return;
-    DrawResult ry = locate<DT>(li, si, ld, sd, has_q, cx.s, cx.V, v1, a.nt, ty, true, sm);
+    // y on wavefront 0 and z on wavefront 1, side by side
+    const float v2 = sm.vs2[a1];
+    const int wave = tid / kWave;
+    if (wave < 2) {
+      const DrawResult r =
+          wave == 0 ? locate_wave<DT>(li, si, ld, sd, has_q, cx.s, cx.V, v1, a.nt, ty, true)
+                    : locate_wave<DT>(lf, sf, li, si, true, cx.s, cx.V, v2, a.nt, tz, true);
+      if ((tid & (kWave - 1)) == 0) sm.pr[wave] = r;
+    }
+    __syncthreads();
+    DrawResult ry = sm.pr[0], rz = sm.pr[1];
+    __syncthreads();
     if (ry.y < 0) ry = draw_tokens<DT>(li, si, nullptr, si, false, cx.s, cx.V, v1, sm);
     cx.write_draw_diag(0, ry);
     const int y = ry.y;
@@ -980,8 +1018,6 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
       cx.write_outputs(a1 + 1, y, a1, a1 + 1);
       return;
     }
-    const float v2 = sm.vs2[a1];
-    DrawResult rz = locate<DT>(lf, sf, li, si, true, cx.s, cx.V, v2, a.nt, tz, true, sm);
     if (rz.y < 0) rz = draw_tokens<DT>(lf, sf, nullptr, sf, false, cx.s, cx.V, v2, sm);
     cx.write_draw_diag(1, rz);
     cx.write_outputs(a1 + 1, rz.y, a1, a1);
