@@ -140,176 +140,201 @@ __device__ __forceinline__ float lane_weight_sum(const float (&xp)[RowT<DT>::VPE
 }
 
 // Sums of the draw weights over tiles [t_begin, t_end) of one row (pair),
-// written to out[t] (coherent device-scope stores when `coherent`).  Each
-// wavefront takes groups of G consecutive tiles; the loads of its next group
-// are issued before the current group is summed (two groups in flight).
+// written to out[t] (device-scope stores, staged in LDS at `stage`, when
+// `coherent`; plain LDS stores otherwise).  Tiles
+// that lie wholly inside the row are read as 16-byte vectors: each wavefront
+// takes groups of G consecutive tiles, and the loads of its next group are in
+// flight while the current group is summed.  Every load of that loop is
+// unconditional (an index past the last whole tile reloads that tile, an
+// absent q row reads the p row), so the compiler waits only for the group it
+// sums.  The ragged last tile, and misaligned rows, go element by element.
 template <int DT>
 __device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
                           const RowStat& qs, bool has_q, float s, int V, int t_begin, int t_end,
-                          float* out, bool coherent) {
+                          float* out, bool coherent, float* stage) {
   constexpr int VPE = RowT<DT>::VPE;
   constexpr int ES = RowT<DT>::ES;
   constexpr int TE = kWave * VPE;
   constexpr int G = kDrawGroup;
   constexpr int stride = kWaves * G;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) |
-                        (has_q ? reinterpret_cast<uintptr_t>(qrow) : 0)) & 15) == 0;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // uniform across the wavefront (scalar), so the tile loop is not divergent
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const char* qsrc = has_q ? qrow : prow;
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(prow) | reinterpret_cast<uintptr_t>(qsrc)) &
+                       15) == 0;
   const float cp = ps.key, isp = ps.inv_S;
   const float cq = has_q ? qs.key : 0.0f, isq = has_q ? qs.inv_S : 0.0f;
+  // sums go to LDS inside the loops (LDS stores do not hold up the wait on
+  // the next group's loads); global sums are copied out afterwards
+  auto put = [&](int t, float v) {
+    if (coherent) stage[t - t_begin] = v;
+    else out[t] = v;
+  };
+  // loop bounds are uniform: keep them scalar so the loops are not divergent
+  t_begin = __builtin_amdgcn_readfirstlane(t_begin);
+  t_end = __builtin_amdgcn_readfirstlane(t_end);
+  const int t_full =
+      __builtin_amdgcn_readfirstlane(vec_ok ? max(t_begin, min(t_end, V / TE)) : t_begin);
 
-  // vector loads of a whole group when it lies inside the row
-  auto fetch = [&](int t0, u32x4 (&vp)[G], u32x4 (&vq)[G]) -> bool {
-    if (!(t0 < t_end && vec_ok && (t0 + G) * TE <= V)) return false;
+  auto fetch = [&](int t0, u32x4 (&vp)[G], u32x4 (&vq)[G]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t off = static_cast<int64_t>((t0 + g) * TE + lane * VPE) * ES;
+      const int t = min(t0 + g, t_full - 1);
+      const int64_t off = static_cast<int64_t>(t * TE + lane * VPE) * ES;
       vp[g] = *reinterpret_cast<const u32x4*>(prow + off);
-      if (has_q) vq[g] = *reinterpret_cast<const u32x4*>(qrow + off);
+      vq[g] = *reinterpret_cast<const u32x4*>(qsrc + off);
     }
-    return true;
   };
-  auto emit = [&](int t0, const float (&sums)[G]) {
+  auto reduce = [&](int t0, const u32x4 (&vp)[G], const u32x4 (&vq)[G]) {
+    float sums[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float xp[VPE], xq[VPE];
+      unpack_vec<DT>(vp[g], xp);
+      unpack_vec<DT>(vq[g], xq);
+      sums[g] = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
+    }
     if (lane == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (t0 + g < t_end) {
-          if (coherent) store_coherent(out + t0 + g, sums[g]);
-          else out[t0 + g] = sums[g];
-        }
-      }
+      for (int g = 0; g < G; ++g)
+        if (t0 + g < t_full) put(t0 + g, sums[g]);
     }
   };
-  // sums of a fetched group, or of a group at the row's edge (element loads)
-  auto reduce = [&](int t0, bool fetched, const u32x4 (&vp)[G], const u32x4 (&vq)[G]) {
-    float sums[G];
-    if (fetched) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float xp[VPE], xq[VPE];
-        unpack_vec<DT>(vp[g], xp);
-        if (has_q) unpack_vec<DT>(vq[g], xq);
-        else
-#pragma unroll
-          for (int q = 0; q < VPE; ++q) xq[q] = 0.0f;
-        sums[g] = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
-      }
-    } else {
-#pragma unroll 1
-      for (int g = 0; g < G; ++g) {
-        float xp[VPE], xq[VPE];
-        const int e = (t0 + g) * TE + lane * VPE;
-        load_group<DT>(prow, e, V, vec_ok, xp);
-        if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
-        else
-#pragma unroll
-          for (int q = 0; q < VPE; ++q) xq[q] = 0.0f;
-        sums[g] = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
-      }
+  if (t_full > t_begin) {
+    int t = t_begin + wave * G;
+    u32x4 ap[G], aq[G], bp[G], bq[G];
+    fetch(t, ap, aq);
+    while (t < t_full) {
+      fetch(t + stride, bp, bq);
+      __builtin_amdgcn_sched_barrier(0);   // the next group's loads go out first
+      reduce(t, ap, aq);
+      t += stride;
+      if (t >= t_full) break;
+      fetch(t + stride, ap, aq);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(t, bp, bq);
+      t += stride;
     }
-    emit(t0, sums);
-  };
-
-  int t = t_begin + wave * G;
-  u32x4 ap[G], aq[G], bp[G], bq[G];
-  bool fa = fetch(t, ap, aq);
-  while (t < t_end) {
-    const bool fb = fetch(t + stride, bp, bq);
-    reduce(t, fa, ap, aq);
-    t += stride;
-    if (t >= t_end) break;
-    fa = fetch(t + stride, ap, aq);
-    reduce(t, fb, bp, bq);
-    t += stride;
+  }
+  // tiles past the whole-vector range: element loads
+  for (int t = t_full + wave; t < t_end; t += kWaves) {
+    float xp[VPE], xq[VPE];
+    const int e = t * TE + lane * VPE;
+    load_group<DT>(prow, e, V, vec_ok, xp);
+    if (has_q) load_group<DT>(qrow, e, V, vec_ok, xq);
+    else
+#pragma unroll
+      for (int q = 0; q < VPE; ++q) xq[q] = 0.0f;
+    const float sum = wave_total(lane_weight_sum<DT>(xp, xq, s, cp, isp, cq, isq, has_q));
+    if (lane == 0) put(t, sum);
+  }
+  if (coherent) {
+    __syncthreads();
+    for (int i = tid; i < t_end - t_begin; i += kThreads) store_coherent(out + t_begin + i, stage[i]);
   }
 }
 
 // The hierarchy's two draws at one position in one pass: over tiles
 // [t_begin, t_end), the weights of y (p = L_i, q = L_d, or L_i alone for the
 // bonus) and of z (p = L_f, q = L_i) are summed per tile from one read of each
-// of the three rows and stored (device-scope) to out_y[t] and out_z[t].
+// of the three rows and stored (device-scope, staged in LDS at `stage`) to
+// out_y[t] and out_z[t].  Same pipelining as tile_pass.
 template <int DT>
 __device__ __forceinline__ void tile_pass_joint(const char* irow, const RowStat& ist,
                                                 const char* drow, const RowStat& dst, bool has_d,
                                                 const char* frow, const RowStat& fst, float s,
                                                 int V, int t_begin, int t_end, float* out_y,
-                                                float* out_z) {
+                                                float* out_z, float* stage) {
   constexpr int VPE = RowT<DT>::VPE;
   constexpr int ES = RowT<DT>::ES;
   constexpr int TE = kWave * VPE;
   constexpr int G = 2;
   constexpr int stride = kWaves * G;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // uniform across the wavefront (scalar), so the tile loop is not divergent
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const char* dsrc = has_d ? drow : irow;
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(irow) | reinterpret_cast<uintptr_t>(frow) |
-                        (has_d ? reinterpret_cast<uintptr_t>(drow) : 0)) & 15) == 0;
+                        reinterpret_cast<uintptr_t>(dsrc)) & 15) == 0;
   const float ci = ist.key, isi = ist.inv_S, cf = fst.key, isf = fst.inv_S;
   const float cd = has_d ? dst.key : 0.0f, isd = has_d ? dst.inv_S : 0.0f;
+  // loop bounds are uniform: keep them scalar so the loops are not divergent
+  t_begin = __builtin_amdgcn_readfirstlane(t_begin);
+  t_end = __builtin_amdgcn_readfirstlane(t_end);
+  const int t_full =
+      __builtin_amdgcn_readfirstlane(vec_ok ? max(t_begin, min(t_end, V / TE)) : t_begin);
 
-  auto fetch = [&](int t0, u32x4 (&vi)[G], u32x4 (&vd)[G], u32x4 (&vf)[G]) -> bool {
-    if (!(t0 < t_end && vec_ok && (t0 + G) * TE <= V)) return false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t off = static_cast<int64_t>((t0 + g) * TE + lane * VPE) * ES;
-      vi[g] = *reinterpret_cast<const u32x4*>(irow + off);
-      vf[g] = *reinterpret_cast<const u32x4*>(frow + off);
-      if (has_d) vd[g] = *reinterpret_cast<const u32x4*>(drow + off);
-    }
-    return true;
-  };
-  auto sums = [&](const float (&xi)[VPE], float (&xd)[VPE], const float (&xf)[VPE], float& sy,
-                  float& sz) {
-    if (!has_d)
-#pragma unroll
-      for (int q = 0; q < VPE; ++q) xd[q] = 0.0f;
+  auto sums = [&](const float (&xi)[VPE], const float (&xd)[VPE], const float (&xf)[VPE],
+                  float& sy, float& sz) {
     sy = wave_total(lane_weight_sum<DT>(xi, xd, s, ci, isi, cd, isd, has_d));
     sz = wave_total(lane_weight_sum<DT>(xf, xi, s, cf, isf, ci, isi, true));
   };
-  auto reduce = [&](int t0, bool fetched, const u32x4 (&vi)[G], const u32x4 (&vd)[G],
-                    const u32x4 (&vf)[G]) {
-    float sy[G], sz[G];
-    if (fetched) {
+  auto fetch = [&](int t0, u32x4 (&vi)[G], u32x4 (&vd)[G], u32x4 (&vf)[G]) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float xi[VPE], xd[VPE], xf[VPE];
-        unpack_vec<DT>(vi[g], xi);
-        unpack_vec<DT>(vf[g], xf);
-        if (has_d) unpack_vec<DT>(vd[g], xd);
-        sums(xi, xd, xf, sy[g], sz[g]);
-      }
-    } else {
-#pragma unroll 1
-      for (int g = 0; g < G; ++g) {
-        float xi[VPE], xd[VPE], xf[VPE];
-        const int e = (t0 + g) * TE + lane * VPE;
-        load_group<DT>(irow, e, V, vec_ok, xi);
-        load_group<DT>(frow, e, V, vec_ok, xf);
-        if (has_d) load_group<DT>(drow, e, V, vec_ok, xd);
-        sums(xi, xd, xf, sy[g], sz[g]);
-      }
+    for (int g = 0; g < G; ++g) {
+      const int t = min(t0 + g, t_full - 1);
+      const int64_t off = static_cast<int64_t>(t * TE + lane * VPE) * ES;
+      vi[g] = *reinterpret_cast<const u32x4*>(irow + off);
+      vf[g] = *reinterpret_cast<const u32x4*>(frow + off);
+      vd[g] = *reinterpret_cast<const u32x4*>(dsrc + off);
+    }
+  };
+  auto reduce = [&](int t0, const u32x4 (&vi)[G], const u32x4 (&vd)[G], const u32x4 (&vf)[G]) {
+    float sy[G], sz[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float xi[VPE], xd[VPE], xf[VPE];
+      unpack_vec<DT>(vi[g], xi);
+      unpack_vec<DT>(vf[g], xf);
+      unpack_vec<DT>(vd[g], xd);
+      sums(xi, xd, xf, sy[g], sz[g]);
     }
     if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (t0 + g < t_end) {
-          store_coherent(out_y + t0 + g, sy[g]);
-          store_coherent(out_z + t0 + g, sz[g]);
+        if (t0 + g < t_full) {
+          stage[2 * (t0 + g - t_begin)] = sy[g];
+          stage[2 * (t0 + g - t_begin) + 1] = sz[g];
         }
       }
     }
   };
-
-  int t = t_begin + wave * G;
-  u32x4 ai[G], ad[G], af[G], bi[G], bd[G], bf[G];
-  bool fa = fetch(t, ai, ad, af);
-  while (t < t_end) {
-    const bool fb = fetch(t + stride, bi, bd, bf);
-    reduce(t, fa, ai, ad, af);
-    t += stride;
-    if (t >= t_end) break;
-    fa = fetch(t + stride, ai, ad, af);
-    reduce(t, fb, bi, bd, bf);
-    t += stride;
+  if (t_full > t_begin) {
+    int t = t_begin + wave * G;
+    u32x4 ai[G], ad[G], af[G], bi[G], bd[G], bf[G];
+    fetch(t, ai, ad, af);
+    while (t < t_full) {
+      fetch(t + stride, bi, bd, bf);
+      __builtin_amdgcn_sched_barrier(0);   // the next group's loads go out first
+      reduce(t, ai, ad, af);
+      t += stride;
+      if (t >= t_full) break;
+      fetch(t + stride, ai, ad, af);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(t, bi, bd, bf);
+      t += stride;
+    }
   }
+  for (int t = t_full + wave; t < t_end; t += kWaves) {
+    float xi[VPE], xd[VPE], xf[VPE];
+    const int e = t * TE + lane * VPE;
+    load_group<DT>(irow, e, V, vec_ok, xi);
+    load_group<DT>(frow, e, V, vec_ok, xf);
+    if (has_d) load_group<DT>(drow, e, V, vec_ok, xd);
+    else
+#pragma unroll
+      for (int q = 0; q < VPE; ++q) xd[q] = 0.0f;
+    float sy, sz;
+    sums(xi, xd, xf, sy, sz);
+    if (lane == 0) {
+      stage[2 * (t - t_begin)] = sy;
+      stage[2 * (t - t_begin) + 1] = sz;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * (t_end - t_begin); i += kThreads)
+    store_coherent((i & 1 ? out_z : out_y) + t_begin + (i >> 1), stage[i]);
 }
 
 // Inverse CDF over NT tile sums (from LDS, or coherent loads from global when
@@ -463,7 +488,7 @@ __device__ __attribute__((noinline)) DrawResult draw_tokens(const char* prow, co
                                   VerifyShared& sm) {
   constexpr int TE = kWave * RowT<DT>::VPE;
   const int NT = (V + TE - 1) / TE;
-  tile_pass<DT>(prow, ps, qrow, qs, has_q, s, V, 0, NT, sm.tiles, false);
+  tile_pass<DT>(prow, ps, qrow, qs, has_q, s, V, 0, NT, sm.tiles, false, nullptr);
   __syncthreads();
   return locate<DT>(prow, ps, qrow, qs, has_q, s, V, v, NT, sm.tiles, false, sm);
 }
@@ -861,7 +886,8 @@ __device__ bool draw_slice(SeqCtx<DT>& cx, int g, int stage, const char* pr, con
   const VerifyArgs& a = cx.a;
   float* tsum = a.tsum[stage] + static_cast<int64_t>(cx.b) * a.nt;
   const int t0 = g * a.tps;
-  tile_pass<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, t0, min(a.nt, t0 + a.tps), tsum, true);
+  tile_pass<DT>(pr, ps, qr, qs, has_q, cx.s, cx.V, t0, min(a.nt, t0 + a.tps), tsum, true,
+                cx.sm.tiles);
   return slice_done(a.cnt[stage] + cx.b, a.ns, cx.sm);
 }
 
@@ -993,7 +1019,7 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
     const RowStat& sd = sm.st[0][has_q ? a1 : 0];
     const RowStat& sf = sm.st[2][a1];
     tile_pass_joint<DT>(li, si, ld, sd, has_q, lf, sf, cx.s, cx.V, t0, min(a.nt, t0 + a.tps),
-                        ty, tz);
+                        ty, tz, sm.tiles);
     if (!slice_done(a.cnt[0] + b, a.ns, sm)) return;
     // y on wavefront 0 and z on wavefront 1, side by side
     const float v2 = sm.vs2[a1];
