@@ -8,7 +8,7 @@
 #include <string>
 
 #include "spec_verify.h"
-#include "sv_common.h"
+#include "sv_args.h"
 
 namespace {
 

@@ -3,7 +3,7 @@
 // KV-cache reuse -- entries of discarded tokens are removed before the next
 // phase, without recomputation -- and on batch inference with paged attention
 // and block tables, which lets each sequence keep its own length unpadded).
-#include "sv_common.h"
+#include "sv_args.h"
 
 namespace sv {
 

@@ -21,7 +21,7 @@
 // fetched from HBM once and served to the other M tiles from that XCD's L2.
 #include <algorithm>
 
-#include "sv_common.h"
+#include "sv_args.h"
 
 namespace sv {
 

@@ -22,7 +22,7 @@
 // summary (section 3.B) and the bonus token its section 2 item 1.
 #pragma once
 
-#include "sv_common.h"
+#include "sv_args.h"
 
 namespace sv {
 
