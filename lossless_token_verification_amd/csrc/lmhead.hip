@@ -30,39 +30,43 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WM = kGemmWM, WN = kGemmWN;  // wavefront grid of a workgroup
-constexpr int FM = kGemmMT / (WM * 32);  // 32 x 32 MFMA tiles per wavefront, rows
-constexpr int FN = kGemmNT / (WN * 32);  // and columns
-constexpr int GT = WM * WN * kWave;    // threads per workgroup
-constexpr int MT = WM * FM * 32;
-constexpr int NT = WN * FN * 32;
-constexpr int KT = kGemmKT;
-constexpr int LROW = KT + 8;           // bf16 per LDS row (16-byte pad against bank conflicts)
-constexpr int VPR = KT / 8;            // 16-byte vectors per tile row
-constexpr int A_PER = MT * VPR / GT;   // A vectors each thread copies per step
-constexpr int B_PER = NT * VPR / GT;
-static_assert(MT == kGemmMT && NT == kGemmNT, "tile sizes");
-static_assert(MT * VPR % GT == 0 && NT * VPR % GT == 0, "copy slots");
+// Tile configuration: MT x NT outputs per workgroup on a WM x WN grid of
+// wavefronts, each holding (MT / WM / 32) x (NT / WN / 32) MFMA tiles.
+template <int MT_, int NT_, int WM_, int WN_>
+struct GemmCfg {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int MT = MT_, NT = NT_;
+  static constexpr int FM = MT / (WM * 32), FN = NT / (WN * 32);
+  static constexpr int GT = WM * WN * kWave;          // threads per workgroup
+  static constexpr int KT = kGemmKT;
+  static constexpr int LROW = KT + 8;                 // bf16 per LDS row (16-byte pad)
+  static constexpr int VPR = KT / 8;                  // 16-byte vectors per tile row
+  static constexpr int A_PER = MT * VPR / GT;         // A vectors each thread copies per step
+  static constexpr int B_PER = NT * VPR / GT;
+  static_assert(FM * WM * 32 == MT && FN * WN * 32 == NT, "tile shape");
+  static_assert(MT * VPR % GT == 0 && NT * VPR % GT == 0, "copy slots");
 
-struct TileShared {
-  alignas(16) uint16_t a[2][MT * LROW];
-  alignas(16) uint16_t b[2][NT * LROW];
+  struct Tiles {
+    alignas(16) uint16_t a[2][MT * LROW];
+    alignas(16) uint16_t b[2][NT * LROW];
+  };
+  struct Epi {
+    float m[WN][MT];
+    int i[WN][MT];
+    float s[WN][MT];
+    float rs[MT];     // log2(e) / temperature of the row (0: greedy)
+    int tok[MT];      // drafted token of the row (-1: none); rows mode: source row
+    float rmax[MT];
+    int ridx[MT];
+  };
+  union Shared {
+    Tiles t;
+    Epi e;            // used after the last K step
+  };
 };
-
-struct EpiShared {
-  float m[WN][MT];
-  int i[WN][MT];
-  float s[WN][MT];
-  float rs[MT];     // log2(e) / temperature of the row (0: greedy)
-  int tok[MT];      // drafted token of the row (-1: none); rows mode: source row
-  float rmax[MT];
-  int ridx[MT];
-};
-
-union GemmShared {
-  TileShared t;
-  EpiShared e;      // used after the last K step
-};
+// statistics over all B(2k+1) rows; recompute of the 2B stopped rows
+using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN>;
+using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN>;
 
 __device__ __forceinline__ const uint16_t* a_row(const GemmArgs& a, int g) {
   return g < a.m_draft ? a.a_draft + static_cast<int64_t>(g) * a.d
@@ -82,11 +86,14 @@ __device__ __forceinline__ void row_meta(const GemmArgs& a, int g, int& b, int& 
   }
 }
 
-template <bool ROWS>
-__global__ __launch_bounds__(GT) void lmhead_gemm(GemmArgs a) {
-  __shared__ GemmShared sh;
-  TileShared& sm = sh.t;
-  EpiShared& ep = sh.e;
+template <class C, bool ROWS>
+__global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
+  constexpr int WN = C::WN, FM = C::FM, FN = C::FN, GT = C::GT;
+  constexpr int MT = C::MT, NT = C::NT, KT = C::KT, LROW = C::LROW, VPR = C::VPR;
+  constexpr int A_PER = C::A_PER, B_PER = C::B_PER;
+  __shared__ typename C::Shared sh;
+  typename C::Tiles& sm = sh.t;
+  typename C::Epi& ep = sh.e;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / WN, wn = wave - wm * WN;
   const int nM = (a.M + MT - 1) / MT;
@@ -376,8 +383,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (lane == 0) a.out[row] = out;
 }
 
+template <class C>
 unsigned gemm_grid(const GemmArgs& a) {
-  const unsigned nM = static_cast<unsigned>((a.M + MT - 1) / MT);
+  const unsigned nM = static_cast<unsigned>((a.M + C::MT - 1) / C::MT);
   const unsigned nN8 = static_cast<unsigned>((a.n_tiles + 7) / 8) * 8u;
   return nM * nN8;
 }
@@ -385,12 +393,14 @@ unsigned gemm_grid(const GemmArgs& a) {
 }  // namespace
 
 hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(lmhead_gemm<false>, dim3(gemm_grid(a)), dim3(GT), 0, st, a);
+  hipLaunchKernelGGL((lmhead_gemm<StatsCfg, false>), dim3(gemm_grid<StatsCfg>(a)),
+                     dim3(StatsCfg::GT), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(lmhead_gemm<true>, dim3(gemm_grid(a)), dim3(GT), 0, st, a);
+  hipLaunchKernelGGL((lmhead_gemm<RowsCfg, true>), dim3(gemm_grid<RowsCfg>(a)),
+                     dim3(RowsCfg::GT), 0, st, a);
   return hipGetLastError();
 }
 
