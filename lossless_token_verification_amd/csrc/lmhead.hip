@@ -68,6 +68,37 @@ struct GemmCfg {
 using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN>;
 using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN>;
 
+// Reductions over each 32-lane half of a wavefront (the lanes holding one
+// output row of a 32 x 32 MFMA tile) with DPP moves on the VALU: a scan within
+// each row of 16 lanes (row_shr 1, 2, 4, 8), then rows 1 and 3 fold in the
+// last lane of rows 0 and 2 (row_bcast 15).  Lane 31 ends with the result of
+// lanes 0..31, lane 63 with that of lanes 32..63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY),
+                                                             __float_as_int(x), CTRL, ROW_MASK,
+                                                             0xf, false)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_step(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf,
+                                                         false));
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = dpp_max_step<0x111, 0xf>(x);
+  x = dpp_max_step<0x112, 0xf>(x);
+  x = dpp_max_step<0x114, 0xf>(x);
+  x = dpp_max_step<0x118, 0xf>(x);
+  return dpp_max_step<0x142, 0xa>(x);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  x = dpp_add_step<0x111, 0xf>(x);
+  x = dpp_add_step<0x112, 0xf>(x);
+  x = dpp_add_step<0x114, 0xf>(x);
+  x = dpp_add_step<0x118, 0xf>(x);
+  return dpp_add_step<0x142, 0xa>(x);
+}
+
 __device__ __forceinline__ const uint16_t* a_row(const GemmArgs& a, int g) {
   return g < a.m_draft ? a.a_draft + static_cast<int64_t>(g) * a.d
                        : a.a_target + static_cast<int64_t>(g - a.m_draft) * a.d;
@@ -240,39 +271,58 @@ __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
     ep.rs[tid] = s;
     ep.tok[tid] = tok;
   }
-  __syncthreads();
+  // greedy rows need the lowest column of the maximum as well
+  const bool any_greedy = __syncthreads_or(tid < MT && m0 + tid < a.M && ep.rs[tid] == 0.0f);
 
-  // pass 1: (max, lowest column) of each row over the tile
+  // pass 1: the maximum of each row over the tile (and its lowest column)
+  if (any_greedy) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      float m = -INFINITY;
-      int idx = 0x7fffffff;
+      for (int q = 0; q < 16; ++q) {
+        float m = -INFINITY;
+        int idx = 0x7fffffff;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = col_of(fn);
-        const float v = acc[fm][fn][q];
-        if (col < a.V && v > m) {
-          m = v;
-          idx = col;
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = col_of(fn);
+          const float v = acc[fm][fn][q];
+          if (col < a.V && v > m) {
+            m = v;
+            idx = col;
+          }
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+          const float om = __shfl_xor(m, o, kWave);
+          const int oi = __shfl_xor(idx, o, kWave);
+          if (om > m || (om == m && oi < idx)) {
+            m = om;
+            idx = oi;
+          }
+        }
+        if (c32 == 0) {
+          const int rl = row_of(fm, q);
+          ep.m[wn][rl] = m;
+          ep.i[wn][rl] = idx;
         }
       }
+  } else {
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) {
-        const float om = __shfl_xor(m, o, kWave);
-        const int oi = __shfl_xor(idx, o, kWave);
-        if (om > m || (om == m && oi < idx)) {
-          m = om;
-          idx = oi;
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          if (col_of(fn) < a.V) m = fmaxf(m, acc[fm][fn][q]);
+        m = half_max(m);
+        if (c32 == 31) {
+          const int rl = row_of(fm, q);
+          ep.m[wn][rl] = m;
+          ep.i[wn][rl] = 0x7fffffff;
         }
       }
-      if (c32 == 0) {
-        const int rl = row_of(fm, q);
-        ep.m[wn][rl] = m;
-        ep.i[wn][rl] = idx;
-      }
-    }
+  }
   __syncthreads();
   if (tid < MT) {
     float m = ep.m[0][tid];
@@ -306,9 +356,8 @@ __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
         if (col < a.V && s > 0.0f) sum += __builtin_amdgcn_exp2f(fmaf(v, s, nc));
         if (col == tok) a.gath[m0 + rl] = v;
       }
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-      if (c32 == 0) ep.s[wn][rl] = sum;
+      sum = half_sum(sum);
+      if (c32 == 31) ep.s[wn][rl] = sum;
     }
   __syncthreads();
   if (tid < MT && m0 + tid < a.M) {
