@@ -285,8 +285,9 @@ def main():
                     help="also run a copy of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into the traffic file and exit")
-    ap.add_argument("--path", choices=("hier", "lmhead"), default="hier",
-                    help="hier: the hierarchical verify + rollback step (default); lmhead: "
+    ap.add_argument("--path", choices=("hier", "hier_lazy", "lmhead"), default="hier",
+                    help="hier: the hierarchical verify + rollback step (default); hier_lazy: "
+                         "the same step reading only the L_f rows stage 2 can reach; lmhead: "
                          "the fused LM-head verify")
     args = ap.parse_args()
     if args.traffic_from:
@@ -328,9 +329,12 @@ def main():
 
     bufs = {}
 
+    lazy = args.path == "hier_lazy"
+    call = sv.spec_verify_hier_rollback_lazy if lazy else sv.spec_verify_hier_rollback
+
     def step(i, events=None):
         # verification of both stages and the paged-KV rollback, one call
-        return sv.spec_verify_hier_rollback(w["ld_logits"], w["li_logits"], w["lf_logits"],
+        return call(w["ld_logits"], w["li_logits"], w["lf_logits"],
                                             w["draft_tokens"], w["temperature"], table, lens,
                                             block_size=w["block_size"], max_freed=1,
                                             window=w["window"], seed=0, offset=i,
@@ -362,6 +366,27 @@ def main():
 
     ms_step = total_ms / args.steps
     k1_avg = sum(k1_ms) / len(k1_ms)
+    if lazy:
+        # bytes actually read: every L_d and L_i row, L_f rows 0..a1 of each sequence
+        a1 = bufs["out"]["accept_len_inter"].cpu()
+        lf_rows = int((a1 + 1).sum())
+        read_bytes = (B * k + B * (k + 1) + lf_rows) * V * 2
+        line = {
+            "metric": "verified draft tokens/s, hierarchical verify with lazy final exit, "
+                      "B=256 k=8 V=128256 bf16",
+            "value": round(B * k / (ms_step / 1e3), 1), "unit": "verified draft tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "hierarchical verify + KV rollback, L_f rows read only up "
+                                   "to each sequence's stage-1 stop", "B": B, "k": k, "V": V},
+            "dense_bytes_per_step": launch_bytes, "read_bytes_per_step": read_bytes,
+            "lf_rows_read": lf_rows, "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
+            "stats_phase_us": round(k1_avg * 1e3, 2),
+            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
+        }
+        print(json.dumps(line), flush=True)
+        return
     value = B * k / (ms_step / 1e3)
     step_gbps = launch_bytes / (ms_step / 1e3) / 1e9
     k1_gbps = launch_bytes / (k1_avg / 1e3) / 1e9

@@ -271,6 +271,27 @@ int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
                                   size_t workspace_bytes, const spec_verify_diag* diag,
                                   void* hip_stream);
 
+/* spec_verify_hier_rollback with a lazy final exit: the L_f rows past each
+ * sequence's stage-1 stop are never read.  Stage 2 only tests tentative tokens
+ * t_0..t_a1, so it reads L_f rows 0..a1 alone (HiSpec summary, section 2
+ * "Kernmechanismus": the intermediate exit discards tokens early, before the
+ * final exit verifies them).  The launches: statistics of every L_d and L_i
+ * row, stage 1 per sequence, statistics of L_f rows 0..a1 only, then the
+ * verification.  Results are bit-identical to spec_verify_hier_rollback's;
+ * the bytes read depend on the data.  Same arguments and workspace. */
+int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t window,
+                                       const void* ld_logits, const void* li_logits,
+                                       const void* lf_logits, const int32_t* draft_tokens,
+                                       const float* temperature, int32_t* accept_len_inter,
+                                       int32_t* accept_len_final, int32_t* out_tokens,
+                                       int32_t* num_emitted, int32_t* num_drop,
+                                       int32_t max_blocks, int32_t block_size,
+                                       int32_t* block_table, int32_t* seq_lens,
+                                       int32_t* freed_blocks, int32_t max_freed,
+                                       int32_t* num_freed, void* workspace,
+                                       size_t workspace_bytes, const spec_verify_diag* diag,
+                                       void* hip_stream);
+
 /* Synchronises hip_stream, then copies the device flags (SV_FLAG_*) of the
  * last verify call that used `workspace` into *flags_out (host). */
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream);

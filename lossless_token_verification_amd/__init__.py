@@ -44,7 +44,7 @@ EXPORTED = (
     "spec_verify_workspace_bytes", "spec_verify_validate", "spec_verify_single",
     "spec_verify_hier", "kv_blocktable_truncate", "spec_verify_hier_rollback",
     "spec_verify_device_status", "spec_verify_lmhead_workspace_bytes",
-    "spec_verify_lmhead_single",
+    "spec_verify_lmhead_single", "spec_verify_hier_rollback_lazy",
 )
 
 
@@ -99,6 +99,8 @@ def library():
     lib.spec_verify_hier_rollback.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P, P, P,
                                               P, P, i32, i32, P, P, P, i32, P, P, sz,
                                               ctypes.POINTER(Diag), P]
+    lib.spec_verify_hier_rollback_lazy.restype = i32
+    lib.spec_verify_hier_rollback_lazy.argtypes = lib.spec_verify_hier_rollback.argtypes
     lib.kv_blocktable_truncate.restype = i32
     lib.kv_blocktable_truncate.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P]
     lib.spec_verify_device_status.restype = i32
@@ -347,7 +349,7 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
 def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
                               block_table, seq_lens, *, block_size, max_freed, window=4,
                               seed=0, offset=0, diag=False, workspace=None, events=None,
-                              out=None):
+                              out=None, _lazy=False):
     """spec_verify_hier plus the paged-KV rollback of block_table / seq_lens
     (in place) in the same launches.  Returns the spec_verify_hier dict plus
     freed_blocks [B, max_freed] and num_freed [B].  ``out``: a dict returned
@@ -383,7 +385,8 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
                 tuple(out["freed_blocks"].shape) != (B, max_freed):
             raise ValueError("out buffers do not match this call's shapes")
     dg = _make_diag(diag, events, B, k, dev, out)
-    _check(lib.spec_verify_hier_rollback(
+    fn = lib.spec_verify_hier_rollback_lazy if _lazy else lib.spec_verify_hier_rollback
+    _check(fn(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
         _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len_inter"]),
         _ptr(out["accept_len_final"]), _ptr(out["out_tokens"]), _ptr(out["num_emitted"]),
@@ -392,6 +395,14 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
         _ptr(out["num_freed"]), _ptr(ws), ws.numel(),
         ctypes.byref(dg) if dg is not None else None, _stream(dev)))
     return out
+
+
+def spec_verify_hier_rollback_lazy(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
+                                   block_table, seq_lens, **kw):
+    """spec_verify_hier_rollback reading only the L_f rows stage 2 can reach
+    (rows 0..a1 of each sequence); bit-identical results."""
+    return spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
+                                     block_table, seq_lens, _lazy=True, **kw)
 
 
 def kv_blocktable_truncate(block_table, seq_lens, num_drop, block_size, max_freed):

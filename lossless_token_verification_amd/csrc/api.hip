@@ -27,7 +27,7 @@ struct Plan {
   int nc = 0;
   int64_t ld = 0;
   size_t ws_bytes = 0;
-  size_t seq_bytes = 0;   // per-sequence slice counters
+  size_t seq_bytes = 0;   // per-sequence slice counters and stage-1 counts
   size_t tile_bytes = 0;  // draw tile sums of both stages
   int nt = 0;             // draw tiles per row
   int ns = 0;             // slices (workgroups) per sequence
@@ -76,7 +76,8 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   p->tps = num_exits == 3 ? sv::kTilesPerSliceJoint : sv::kTilesPerSlice;
   p->ns = (p->nt + p->tps - 1) / p->tps;
   if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
-  p->seq_bytes = (static_cast<size_t>(B) * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  // two slice counters and the lazy final exit's stage-1 counts
+  p->seq_bytes = (static_cast<size_t>(B) * 3 * sizeof(int32_t) + 255) / 256 * 256;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
   p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes +
                 static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
@@ -151,12 +152,43 @@ int32_t check_kv(int32_t batch, int32_t max_blocks, int32_t block_size, const in
   return SV_OK;
 }
 
+// Arguments of the lazy final exit's stage-1 pass: one workgroup per
+// sequence decides stage 1 from the L_d and L_i statistics.
+sv::VerifyArgs stage1_args(const spec_verify_desc* desc, const Plan& p, const void* const* logits,
+                           const sv::Partial* partials, const int32_t* tokens,
+                           const float* temperature, uint32_t* flags) {
+  sv::VerifyArgs va{};
+  va.hier = 1;
+  va.B = desc->batch;
+  va.k = desc->num_draft;
+  va.V = desc->vocab;
+  va.dtype = desc->dtype;
+  va.nc = p.nc;
+  va.window = 1;
+  va.nt = p.nt;
+  va.ns = 1;
+  va.tps = p.tps;
+  va.ld = p.ld;
+  for (int e = 0; e < 3; ++e) {
+    va.exit_ptr[e] = logits[e];
+    va.exit_row0[e] = p.exit_row0[e];
+  }
+  va.partials = partials;
+  va.tokens = tokens;
+  va.temperature = temperature;
+  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  va.offset = desc->offset;
+  va.flags = flags;
+  return va;
+}
+
 int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t window,
                    const void* const* logits, const int32_t* tokens, const float* temperature,
                    int32_t* accept_len, int32_t* accept_len_final, int32_t* out_tokens,
                    int32_t* num_emitted, int32_t* num_drop, int32_t* packed, int32_t* cu_offsets,
                    void* workspace, size_t workspace_bytes, const spec_verify_diag* diag,
-                   void* hip_stream, const KvRollback* kv = nullptr) {
+                   void* hip_stream, const KvRollback* kv = nullptr, bool lazy = false) {
   Plan p;
   SV_TRY(make_plan(desc, num_exits, &p));
   if (num_exits == 3 && window < 1) return fail(SV_ERR_INVALID_ARG, "window < 1");
@@ -208,18 +240,40 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.clear_words = seqw;   // slice counters
   sa.n_clear = 2 * B;
   sa.flags = flags;
+  int32_t* lazy_a1 = lazy ? seqw + 2 * B : nullptr;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
     if (err != hipSuccess) return device_error(err, "event record");
   }
-  err = sv::launch_stats(sa, p.rows_total, st);
-  if (err != hipSuccess) return device_error(err, "row statistics launch");
+  if (!lazy) {
+    err = sv::launch_stats(sa, p.rows_total, st);
+    if (err != hipSuccess) return device_error(err, "row statistics launch");
+  } else {
+    // L_d and L_i rows, stage 1 alone, then the L_f rows stage 2 can reach
+    err = sv::launch_stats(sa, p.exit_row0[2], st);
+    if (err != hipSuccess) return device_error(err, "row statistics launch");
+  }
+  sv::VerifyArgs va{};
+  if (lazy) {
+    va = stage1_args(desc, p, logits, partials, tokens, temperature, flags);
+    va.stage1_only = 1;
+    va.lazy_a1 = lazy_a1;
+    err = sv::launch_verify(va, st);
+    if (err != hipSuccess) return device_error(err, "stage-1 launch");
+    sv::StatsArgs sf = sa;
+    sf.row_begin = p.exit_row0[2];
+    sf.n_clear = 0;
+    sf.lazy_a1 = lazy_a1;
+    err = sv::launch_stats(sf, p.rows_total - p.exit_row0[2], st);
+    if (err != hipSuccess) return device_error(err, "final-exit statistics launch");
+  }
   if (diag && diag->stats_end) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
     if (err != hipSuccess) return device_error(err, "event record");
   }
 
-  sv::VerifyArgs va{};
+  va = sv::VerifyArgs{};
+  va.lazy_a1 = lazy_a1;
   va.hier = num_exits == 3;
   va.B = B;
   va.k = desc->num_draft;
@@ -590,6 +644,25 @@ int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
   return run_lmhead(desc, hidden, h_draft, h_target, w_vocab, draft_tokens, temperature,
                     accept_len, out_tokens, num_emitted, num_drop, packed_tokens, cu_offsets,
                     workspace, workspace_bytes, diag, hip_stream);
+}
+
+int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t window,
+                                       const void* ld_logits, const void* li_logits,
+                                       const void* lf_logits, const int32_t* draft_tokens,
+                                       const float* temperature, int32_t* accept_len_inter,
+                                       int32_t* accept_len_final, int32_t* out_tokens,
+                                       int32_t* num_emitted, int32_t* num_drop,
+                                       int32_t max_blocks, int32_t block_size,
+                                       int32_t* block_table, int32_t* seq_lens,
+                                       int32_t* freed_blocks, int32_t max_freed,
+                                       int32_t* num_freed, void* workspace,
+                                       size_t workspace_bytes, const spec_verify_diag* diag,
+                                       void* hip_stream) {
+  const void* logits[3] = {ld_logits, li_logits, lf_logits};
+  KvRollback kv{max_blocks, block_size, max_freed, block_table, seq_lens, freed_blocks, num_freed};
+  return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
+                    accept_len_final, out_tokens, num_emitted, num_drop, nullptr, nullptr,
+                    workspace, workspace_bytes, diag, hip_stream, &kv, true);
 }
 
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream) {

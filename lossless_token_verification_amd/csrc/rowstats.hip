@@ -1,7 +1,8 @@
 // The HBM stream: partial softmax statistics of every 64 KiB chunk of every
-// logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk);
-// the first workgroups also clear the slice counters of the verification
-// stages that follow on the same stream.
+// logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk) of
+// the launch's rows; the first workgroups also clear the slice counters of the
+// verification that follows on the same stream.  With a lazy final exit, the
+// L_f rows past each sequence's stage-1 stop are skipped.
 #include "sv_stats.h"
 
 namespace sv {
@@ -19,13 +20,15 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
     if (i < a.n_clear) a.clear_words[i] = 0;
     if (i == 0) a.flags[0] = 0u;
   }
-  const int row = blockIdx.x / a.nc;
-  const int chunk = blockIdx.x - row * a.nc;
+  const int rel = blockIdx.x / a.nc;
+  const int chunk = blockIdx.x - rel * a.nc;
+  const int row = a.row_begin + rel;
   int e = 0;
   if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
   if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
   const int local = row - a.exit_row0[e];
   const int b = local / a.exit_pos[e];
+  if (a.lazy_a1 && e == 2 && local - b * a.exit_pos[2] > a.lazy_a1[b]) return;
   const float tau = a.temperature ? a.temperature[b] : 1.0f;
   const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
   const float s = greedy ? 0.0f : kLog2e / tau;

@@ -58,6 +58,11 @@ struct VerifyArgs {
   int64_t draw_ld;
   int32_t decide_only;
   int32_t* stop_rows;
+  // Lazy final exit: a first pass with `stage1_only` writes each sequence's
+  // stage-1 accept count to lazy_a1; the verification then merges only the
+  // L_f rows 0..a1 (the only ones stage 2 reads).  NULL: every row.
+  int32_t stage1_only;
+  int32_t* lazy_a1;
   // optional paged-KV rollback of every sequence once its result is known
   int32_t* kv_table;       // [B, kv_max_blocks] or NULL
   int32_t* kv_lens;        // [B]

@@ -49,6 +49,10 @@ struct StatsArgs {
   int32_t* clear_words;    // zeroed by the first workgroups (slice counters)
   int32_t n_clear;
   uint32_t* flags;
+  int32_t row_begin;       // first row of this launch (rows are launched in order)
+  // Lazy final exit: skip L_f row j of sequence b when j > a1[b] (stage 1
+  // stopped before it, so stage 2 never reads it); NULL: every row.
+  const int32_t* lazy_a1;
 };
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);

@@ -955,8 +955,18 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
       d[0] = d[1] = NAN;
     }
   }
+  if (a.stage1_only) {
+    // lazy final exit, first pass: stage 1 alone, from L_d and L_i
+    if (!first) return;
+    cx.pregather(2);
+    cx.merge_all(k, k + 1, 0);
+    const int s1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1, false);
+    if (tid == 0) a.lazy_a1[b] = s1;
+    return;
+  }
   cx.pregather(a.hier ? 3 : 2);
-  cx.merge_all(k, k + 1, a.hier ? k + 1 : 0);
+  // stage 2 reads L_f rows 0..a1 only (all of them unless the final exit is lazy)
+  cx.merge_all(k, k + 1, a.hier ? (a.lazy_a1 ? a.lazy_a1[b] + 1 : k + 1) : 0);
   int a1, a2p;
   float v1;
   if (a.hier) {

@@ -31,7 +31,7 @@ def sv():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(sv.EXPORTED)
     lib = ctypes.CDLL(sv.LIB_PATH)
     for n in names:
@@ -48,7 +48,7 @@ def test_version_and_status_strings(sv):
 
 
 def test_workspace_size_formula(sv):
-    # 256 B of flags + 8 B per sequence + 2 draw-tile sums per (sequence, tile)
+    # 256 B of flags + 12 B per sequence + 2 draw-tile sums per (sequence, tile)
     # (each area padded to 256 B) + one 16-byte partial per (row, 64 KiB chunk)
     def pad(n):
         return (n + 255) // 256 * 256
@@ -56,11 +56,11 @@ def test_workspace_size_formula(sv):
     def tiles(V, per):
         return -(-V // per)
     assert sv.workspace_bytes(256, 8, 128256, 1, 3) == \
-        256 + pad(256 * 8) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
+        256 + pad(256 * 12) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
     assert sv.workspace_bytes(64, 4, 32000, 1, 2) == \
-        256 + pad(64 * 8) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
+        256 + pad(64 * 12) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
     assert sv.workspace_bytes(32, 5, 151936, 0, 2) == \
-        256 + pad(32 * 8) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
+        256 + pad(32 * 12) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 

@@ -1,0 +1,85 @@
+"""GPU parity of the lazy final exit: spec_verify_hier_rollback_lazy reads only
+the L_f rows stage 2 can reach and must give bit-identical results to the
+dense call (and match the oracle, whose hierarchy never looks at L_f past a1)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+KEYS = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop",
+        "freed_blocks", "num_freed")
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lossless_token_verification_amd as m
+    m.library()
+    return m
+
+
+def _both(sv, w, seed, offset, window, ws=None):
+    g = P.to_device(w, DEV)
+    outs = []
+    for fn in (sv.spec_verify_hier_rollback, sv.spec_verify_hier_rollback_lazy):
+        table, lens = g["block_table"].clone(), g["seq_lens"].clone()
+        o = fn(g["ld_logits"], g["li_logits"], g["lf_logits"], g["draft_tokens"],
+               g["temperature"], table, lens, block_size=w["block_size"], max_freed=2,
+               window=window, seed=seed, offset=offset, diag=True, workspace=ws)
+        o["table"], o["lens"] = table, lens
+        outs.append(o)
+    torch.cuda.synchronize()
+    return outs
+
+
+CASES = [
+    # (B, k, V, dtype, temps, window)
+    (12, 8, 50021, "bf16", (1.0,), 4),
+    (8, 6, 20011, "f32", (0.0, 0.7, 1.0), 4),
+    (6, 5, 3001, "bf16", (1.0,), 1),           # misaligned rows
+    (4, 3, 9000, "f32", (0.9,), 2),
+    (3, 0, 5000, "bf16", (1.0,), 4),           # k = 0
+    (5, 8, 4096, "bf16", (1.0,), 4),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}w{c[5]}")
+def test_lazy_equals_dense_and_oracle(sv, case):
+    B, k, V, dt, temps, window = case
+    report = {}
+    for trial in range(3):
+        w = workloads.make_hier(B, k, V, dtype=dt, temps=temps, window=window,
+                                seed=(81, B, k, V, trial), ctx=(16, 64))
+        dense, lazy = _both(sv, w, trial + 2, trial, window)
+        for key in KEYS + ("table", "lens"):
+            assert torch.equal(dense[key], lazy[key]), key
+        ref = P.oracle_hier(w, trial + 2, trial, window)
+        P.compare(lazy, ref, KEYS[:5], range(B), dt == "bf16", report)
+    print(f"lazy {case}: {report}")
+
+
+def test_lazy_and_dense_alternate_on_one_workspace(sv):
+    """Stale statistics of rows the lazy call skips never leak into a result."""
+    w1 = workloads.make_hier(16, 8, 30000, dtype="bf16", seed=(82, 0), ctx=(16, 64))
+    w2 = workloads.make_hier(16, 8, 30000, dtype="bf16", seed=(82, 1), ctx=(16, 64))
+    ws = sv.alloc_workspace(sv.workspace_bytes(16, 8, 30000, torch.bfloat16, 3), DEV)
+    for w in (w1, w2, w1):
+        dense, lazy = _both(sv, w, 5, 1, 4, ws=ws)
+        for key in KEYS + ("table", "lens"):
+            assert torch.equal(dense[key], lazy[key]), key
+
+
+def test_full_size_lazy_equals_dense(sv):
+    w = workloads.make("hier", 0, device=DEV)
+    dense, lazy = _both(sv, w, 0, 3, w["window"])
+    for key in KEYS + ("table", "lens"):
+        assert torch.equal(dense[key], lazy[key]), key
+    a1 = lazy["accept_len_inter"].cpu().numpy()
+    print("full size lazy: mean a1", a1.mean(), "L_f rows read per sequence", (a1 + 1).mean())
