@@ -32,13 +32,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Tile configuration: MT x NT outputs per workgroup on a WM x WN grid of
 // wavefronts, each holding (MT / WM / 32) x (NT / WN / 32) MFMA tiles.
-template <int MT_, int NT_, int WM_, int WN_>
+template <int MT_, int NT_, int WM_, int WN_, int KT_>
 struct GemmCfg {
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int MT = MT_, NT = NT_;
   static constexpr int FM = MT / (WM * 32), FN = NT / (WN * 32);
   static constexpr int GT = WM * WN * kWave;          // threads per workgroup
-  static constexpr int KT = kGemmKT;
+  static constexpr int KT = KT_;
   static constexpr int LROW = KT + 8;                 // bf16 per LDS row (16-byte pad)
   static constexpr int VPR = KT / 8;                  // 16-byte vectors per tile row
   static constexpr int A_PER = MT * VPR / GT;         // A vectors each thread copies per step
@@ -65,8 +65,8 @@ struct GemmCfg {
   };
 };
 // statistics over all B(2k+1) rows; recompute of the 2B stopped rows
-using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN>;
-using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN>;
+using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
+using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
 
 // Reductions over each 32-lane half of a wavefront (the lanes holding one
 // output row of a 32 x 32 MFMA tile) with DPP moves on the VALU: a scan within
