@@ -35,6 +35,8 @@ verify     batched single-stage and hierarchical (L_d -> L_i -> L_f) verify.
 blocktable paged-KV block-table / length rollback.
 lmhead     logits of a linear LM head (hidden . W^T, float64) fed to the
            single-stage verify.
+byproducts row entropies and the verification-outcome export (acceptance
+           probability and largest residual tokens per tested position).
 
 Parity status: every function here is pinned by a CPU test (tests/test_oracle_*)
 except the 4x32 *constants* of Philox, which no library in the CPU container
@@ -42,4 +44,4 @@ exposes; their round structure is pinned through the 4x64 instantiation
 against ``numpy.random.Philox`` and the constants are the published ones.
 """
 
-from . import philox, numerics, rule, verify, blocktable  # noqa: F401
+from . import philox, numerics, rule, verify, blocktable, byproducts  # noqa: F401
