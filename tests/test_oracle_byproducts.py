@@ -17,8 +17,10 @@ import scipy.stats
 from oracle import byproducts, rule, numerics
 from tests.exact_law import law_single, random_dist
 
+
 def _binary_entropy(x):
     return -x * np.log(x) - (1 - x) * np.log1p(-x)
+
 
 @pytest.mark.parametrize("V", [1, 7, 1024, 128256])
 @pytest.mark.parametrize("tau", [0.5, 1.0, 3.0])
@@ -26,6 +28,7 @@ def test_constant_row_has_log_v(V, tau):
     row = np.full(V, 2.5, dtype=np.float32)
     H = byproducts.entropy(numerics.row_distribution(numerics.decode(row), tau))
     assert H == pytest.approx(np.log(V), rel=1e-12, abs=1e-12)
+
 
 @pytest.mark.parametrize("n,gap,tau", [(1, 1.0, 1.0), (5, 2.0, 0.7), (64, -3.0, 1.3), (500, 0.25, 2.0)])
 def test_two_level_row_closed_form(n, gap, tau):
@@ -35,6 +38,7 @@ def test_two_level_row_closed_form(n, gap, tau):
     p_hi = 1.0 / (1.0 + np.exp(-gap / tau))
     assert H == pytest.approx(np.log(n) + _binary_entropy(p_hi), rel=1e-12, abs=1e-12)
 
+
 def test_matches_scipy_on_random_rows():
     rng = np.random.default_rng(3)
     for V, tau in [(10, 1.0), (1000, 0.7), (32000, 1.0), (4096, 2.5)]:
@@ -43,12 +47,14 @@ def test_matches_scipy_on_random_rows():
         ref = scipy.stats.entropy(scipy.special.softmax(row.astype(np.float64) / tau))
         assert H == pytest.approx(ref, rel=1e-10, abs=1e-12)
 
+
 def test_greedy_and_limits():
     row = np.array([0.0, 3.0, 1.0, 3.0, -2.0])
     assert byproducts.entropy(numerics.row_distribution(row, 0.0)) == 0.0
     # tau -> 0+: the two tied maxima share the mass; tau -> inf: uniform
     assert byproducts.entropy(numerics.row_distribution(row, 1e-3)) == pytest.approx(np.log(2), abs=1e-9)
     assert byproducts.entropy(numerics.row_distribution(row, 1e6)) == pytest.approx(np.log(5), abs=1e-6)
+
 
 def test_row_entropies_layout_and_temperature():
     """Row (b, j) has two levels with gap (b + 1) * (j + 1) / 4; sequence b's
@@ -72,6 +78,7 @@ def test_row_entropies_layout_and_temperature():
     assert np.allclose(byproducts.row_entropies(x, None)[1], [
         np.log(half) + _binary_entropy(1 / (1 + np.exp(-2 * (j + 1) / 4))) for j in range(n)])
 
+
 @pytest.mark.parametrize("seed", range(6))
 def test_exact_law_of_position_zero(seed):
     """beta is the exact probability that the rule accepts a draft from Q, and
@@ -94,6 +101,7 @@ def test_exact_law_of_position_zero(seed):
         assert m == pytest.approx(float(p), abs=1e-14)
     assert np.all(mass[len(expect):] == 0) and np.all(tok[len(expect):] == -1)
 
+
 def test_total_variation_identity():
     rng = np.random.default_rng(11)
     for V in (3, 100, 5000):
@@ -102,6 +110,7 @@ def test_total_variation_identity():
         assert byproducts.accept_mass(P, Q) == pytest.approx(1 - 0.5 * np.abs(P - Q).sum(), abs=1e-12)
         _, mass = byproducts.residual_top(P, Q, V)
         assert mass.sum() == pytest.approx(1 - byproducts.accept_mass(P, Q), abs=1e-12)
+
 
 def test_identical_and_disjoint():
     P = np.array([0.5, 0.25, 0.0, 0.25])
@@ -113,11 +122,13 @@ def test_identical_and_disjoint():
     tok, mass = byproducts.residual_top(P, Q, 4)
     assert list(tok) == [0, 1, 3, -1] and list(mass) == [0.5, 0.25, 0.25, 0.0]
 
+
 def test_ties_go_to_the_lower_index():
     P = np.array([0.1, 0.2, 0.1, 0.2, 0.4])
     Q = np.array([0.0, 0.0, 0.0, 0.0, 1.0])
     tok, _ = byproducts.residual_top(P, Q, 3)
     assert list(tok) == [1, 3, 0]
+
 
 def test_outcome_export_layout():
     """Greedy sequences make every entry exact: beta = [argmax Q == argmax P]
@@ -152,6 +163,7 @@ def test_outcome_export_layout():
     beta1, tok1, _ = byproducts.outcome_export(exits[:2], taus, m)
     assert np.array_equal(beta1[:, 0], beta[:, 0], equal_nan=True)
     assert np.all(np.isnan(beta1[:, 1])) and np.all(tok1[:, 1] == -1)
+
 
 def test_planted_mistake_is_detected(monkeypatch):
     """A swapped min/max in the acceptance mass breaks the exact-law pin."""
