@@ -131,7 +131,7 @@ def _ids(rows):
     """Dispatch ids of the row-statistics kernel, and of the calibration copy
     (the last three dispatches of the process)."""
     names = {i: n for i, n, _, _ in rows}
-    stats = {i for i, n in names.items() if "rowstats_kernel<1>" in n}
+    stats = {i for i, n in names.items() if "rowstats_kernel<1, false>" in n}
     last = sorted(names)[-3:]
     if len({names[i] for i in last}) != 1 or any(i in stats for i in last):
         raise SystemExit("the last three dispatches are not the calibration copy")
@@ -289,6 +289,10 @@ def main():
                     help="hier: the hierarchical verify + rollback step (default); hier_lazy: "
                          "the same step reading only the L_f rows stage 2 can reach; lmhead: "
                          "the fused LM-head verify")
+    ap.add_argument("--byproducts", choices=("none", "entropy", "outcome", "all"), default="none",
+                    help="hier path only: also compute the row entropies, the outcome export "
+                         "(acceptance mass and the 8 largest residual tokens per position), "
+                         "or both, in every step")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -331,15 +335,19 @@ def main():
 
     lazy = args.path == "hier_lazy"
     call = sv.spec_verify_hier_rollback_lazy if lazy else sv.spec_verify_hier_rollback
+    if lazy and args.byproducts != "none":
+        raise SystemExit("by-products need every row streamed: use --path hier")
+    extra = dict(entropy=args.byproducts in ("entropy", "all"),
+                 outcome=args.byproducts in ("outcome", "all"))
+    extra["top_m"] = 8 if extra["outcome"] else 0
 
     def step(i, events=None):
         # verification of both stages and the paged-KV rollback, one call
         return call(w["ld_logits"], w["li_logits"], w["lf_logits"],
-                                            w["draft_tokens"], w["temperature"], table, lens,
-                                            block_size=w["block_size"], max_freed=1,
-                                            window=w["window"], seed=0, offset=i,
-                                            workspace=ws, events=events,
-                                            out=bufs.get("out"))
+                    w["draft_tokens"], w["temperature"], table, lens,
+                    block_size=w["block_size"], max_freed=1,
+                    window=w["window"], seed=0, offset=i,
+                    workspace=ws, events=events, out=bufs.get("out"), **extra)
 
     table, lens = table0.clone(), lens0.clone()
     bufs["out"] = step(999999)
@@ -383,6 +391,30 @@ def main():
             "dense_bytes_per_step": launch_bytes, "read_bytes_per_step": read_bytes,
             "lf_rows_read": lf_rows, "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
             "stats_phase_us": round(k1_avg * 1e3, 2),
+            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
+        }
+        print(json.dumps(line), flush=True)
+        return
+    if args.byproducts != "none":
+        k1_gbps = launch_bytes / (k1_avg / 1e3) / 1e9
+        name = {"entropy": "row entropies", "outcome": "outcome export (top 8)",
+                "all": "row entropies and outcome export (top 8)"}[args.byproducts]
+        line = {
+            "metric": f"verified draft tokens/s with {name}, hierarchical verify + KV "
+                      "rollback, B=256 k=8 V=128256 bf16",
+            "value": round(B * k / (ms_step / 1e3), 1), "unit": "verified draft tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"hierarchical verify + KV rollback with {name}",
+                       "B": B, "k": k, "V": V},
+            "roofline": {"bound": "hbm",
+                         "kernel": "rowstats_kernel<bf16, entropy>" if extra["entropy"]
+                         else "rowstats_kernel<bf16>",
+                         "achieved": round(k1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "bytes_per_launch": launch_bytes,
+                         "avg_launch_us": round(k1_avg * 1e3, 2)},
             "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         }
         print(json.dumps(line), flush=True)

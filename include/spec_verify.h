@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 1
+#define SPEC_VERIFY_ABI_VERSION 2
 
 /* Status codes. */
 #define SV_OK 0
@@ -98,6 +98,7 @@ extern "C" {
 #define SV_MAX_DRAFT 63        /* k + 1 positions fit one 64-lane wavefront */
 #define SV_MAX_VOCAB (1 << 20) /* inverse-CDF tile sums stay in LDS          */
 #define SV_MAX_HIDDEN (1 << 16) /* hidden size of the LM-head path            */
+#define SV_MAX_TOP_M 8          /* residual tokens per position in the export */
 
 /* Device flags (spec_verify_device_status). */
 #define SV_FLAG_TOKEN_RANGE 1u /* a drafted token outside [0, V) was rejected        */
@@ -114,10 +115,35 @@ typedef struct {
   uint32_t reserved;  /* must be 0                                             */
 } spec_verify_desc;
 
-/* Optional per-call diagnostics, for parity checks.  Every field is a device
- * pointer (or, for the events, a hipEvent_t handle) or NULL.  Entries that do
- * not apply (untested positions, stages without a draw) are NaN.  Stage index 0 = single stage / hierarchy stage 1,
- * 1 = hierarchy stage 2. */
+/* Optional per-call diagnostics and by-products.  Every field is a device
+ * pointer (or, for the events, a hipEvent_t handle) or NULL; a NULL field is
+ * not computed.  Entries that do not apply (untested positions, stages
+ * without a draw) are NaN.  Stage index 0 = single stage / hierarchy stage 1,
+ * 1 = hierarchy stage 2.
+ *
+ * By-products (spec_verify_single, spec_verify_hier, spec_verify_hier_rollback;
+ * the lazy and LM-head calls return SV_ERR_UNSUPPORTED when one is set):
+ *   entropy   the Shannon entropy in nats of every streamed row's distribution
+ *             (softmax at the sequence's temperature; 0 for greedy sequences),
+ *             rows in the workspace's order: exit 0 [B, k], then exit 1
+ *             [B, k+1], then exit 2 [B, k+1].  The entropy of the draft's
+ *             distribution is what entropy-driven adaptive draft lengths use
+ *             ("Optimierung der Inferenzgeschwindigkeit von Sprachmodellen
+ *             durch spekulative Dekodierung", mind-verse.de, paragraphs on
+ *             SVIP).  It costs one multiply-add per streamed element.
+ *   accept_mass, residual_tokens, residual_mass: the verification-outcome
+ *             export of every tested position (q, p) = (draft or L_d, target
+ *             or L_i) row j < k for stage 0 and (L_i, L_f) row j <= k for
+ *             stage 1: beta = sum_v min(p_v, q_v), the probability that the
+ *             rule accepts there, and the top_m largest r_v of the residual
+ *             r = max(0, p - q) (ties: lower token first; r_v > 0 only;
+ *             padded with token -1, mass 0), r_v being the probability of
+ *             rejecting there and emitting v.  These are the likely outcomes
+ *             of a verification that a speculation cache prepares for
+ *             ("Speculative Speculative Decoding", gist.science 2603.03251,
+ *             section 2 items 1-2, section 3.A and 3.B).  It re-reads the
+ *             rows of every tested position once more after the statistics.
+ */
 typedef struct {
   float* uniforms;   /* [B, 2, k+1, 2]: (u, v) of each position                   */
   double* probs;     /* [B, 2, k+1, 2]: (p(t_j), q(t_j)) of each tested position    */
@@ -125,6 +151,11 @@ typedef struct {
   void* stats_begin; /* hipEvent_t recorded on hip_stream right before the
                         row-statistics kernel (the HBM stream), or NULL          */
   void* stats_end;   /* hipEvent_t recorded right after it, or NULL               */
+  float* entropy;    /* [rows of every exit]: row entropies, nats                */
+  float* accept_mass;          /* [B, 2, k+1]: beta of each tested position      */
+  int32_t* residual_tokens;    /* [B, 2, k+1, top_m]: largest residual tokens    */
+  float* residual_mass;        /* [B, 2, k+1, top_m]: their r_v                  */
+  int32_t top_m;               /* 1..SV_MAX_TOP_M when either residual field is set */
 } spec_verify_diag;
 
 /* Version of this header's ABI (SPEC_VERIFY_ABI_VERSION). */
@@ -137,7 +168,10 @@ const char* spec_verify_status_string(int32_t status);
 const char* spec_verify_last_error(void);
 
 /* Workspace bytes a call needs: num_exits = 2 (spec_verify_single) or 3
- * (spec_verify_hier).  0 if the descriptor is invalid.  Pure host code. */
+ * (spec_verify_hier).  It holds the flag word, per-sequence counters, draw
+ * tile sums, the chunk partials of every row and the by-products' scratch
+ * (entropy partials, outcome-export partials).  0 if the descriptor is
+ * invalid.  Pure host code. */
 size_t spec_verify_workspace_bytes(const spec_verify_desc* desc, int32_t num_exits);
 
 /* Host-side validation of a descriptor, window and workspace size, exactly as

@@ -37,6 +37,7 @@ SV_FLAG_TEMPERATURE = 2
 MAX_DRAFT = 63
 MAX_VOCAB = 1 << 20
 MAX_HIDDEN = 1 << 16
+MAX_TOP_M = 8
 
 # Every symbol include/spec_verify.h declares.
 EXPORTED = (
@@ -58,7 +59,9 @@ class Desc(ctypes.Structure):
 class Diag(ctypes.Structure):
     _fields_ = [("uniforms", ctypes.c_void_p), ("probs", ctypes.c_void_p),
                 ("draws", ctypes.c_void_p), ("stats_begin", ctypes.c_void_p),
-                ("stats_end", ctypes.c_void_p)]
+                ("stats_end", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
+                ("accept_mass", ctypes.c_void_p), ("residual_tokens", ctypes.c_void_p),
+                ("residual_mass", ctypes.c_void_p), ("top_m", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -202,10 +205,13 @@ def _diag_buffers(B, k, device):
                 draws=torch.empty((B, 2, 4), dtype=torch.float64, device=device))
 
 
-def _make_diag(diag, events, B, k, dev, out):
+def _make_diag(diag, events, B, k, dev, out, rows=0, entropy=False, outcome=False, top_m=0):
     """Diag struct: export buffers when ``diag``; ``events`` = (begin, end)
-    hipEvent_t handles (ints) recorded around the row-statistics kernel."""
-    if not diag and events is None:
+    hipEvent_t handles (ints) recorded around the row-statistics kernel;
+    by-product outputs when ``entropy`` (out["entropy"], one float per row of
+    every exit) or ``outcome`` (out["accept_mass"] [B, 2, k+1] and, for
+    top_m > 0, out["residual_tokens"] / out["residual_mass"] [B, 2, k+1, top_m])."""
+    if not diag and events is None and not entropy and not outcome:
         return None
     dg = Diag()
     if diag:
@@ -215,6 +221,20 @@ def _make_diag(diag, events, B, k, dev, out):
                                            bufs["draws"].data_ptr())
     if events is not None:
         dg.stats_begin, dg.stats_end = events
+    if entropy:
+        out["entropy"] = torch.empty((max(1, rows),), dtype=torch.float32, device=dev)
+        dg.entropy = out["entropy"].data_ptr()
+    if outcome:
+        out["accept_mass"] = torch.empty((B, 2, k + 1), dtype=torch.float32, device=dev)
+        dg.accept_mass = out["accept_mass"].data_ptr()
+        if top_m:
+            out["residual_tokens"] = torch.empty((B, 2, k + 1, top_m), dtype=torch.int32,
+                                                 device=dev)
+            out["residual_mass"] = torch.empty((B, 2, k + 1, top_m), dtype=torch.float32,
+                                               device=dev)
+            dg.residual_tokens = out["residual_tokens"].data_ptr()
+            dg.residual_mass = out["residual_mass"].data_ptr()
+            dg.top_m = int(top_m)
     return dg
 
 
@@ -229,10 +249,12 @@ def _prep_common(draft_tokens, temperature, B, k, device):
 
 
 def spec_verify_single(draft_logits, target_logits, draft_tokens, temperature=None, *, seed=0,
-                       offset=0, packed=False, diag=False, workspace=None, events=None):
+                       offset=0, packed=False, diag=False, workspace=None, events=None,
+                       entropy=False, outcome=False, top_m=0):
     """Single-stage verify (standard rule).  Returns a dict of device tensors:
     accept_len, out_tokens [B, k+1] (-1 padded), num_emitted, num_drop, and
-    packed_tokens / cu_offsets and diag buffers when asked.  Asynchronous."""
+    packed_tokens / cu_offsets, diag buffers and by-products (``entropy``,
+    ``outcome`` with ``top_m``, see ``_make_diag``) when asked.  Asynchronous."""
     lib = library()
     B, k, V = draft_logits.shape
     dev = draft_logits.device
@@ -250,7 +272,7 @@ def spec_verify_single(draft_logits, target_logits, draft_tokens, temperature=No
     if packed:
         out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
         out["cu_offsets"] = _int_out((B + 1,), dev)
-    dg = _make_diag(diag, events, B, k, dev, out)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m)
     _check(lib.spec_verify_single(
         ctypes.byref(desc), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
@@ -273,7 +295,7 @@ def _bf16_rows(t, name, shape, device):
 
 def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperature=None, *,
                               seed=0, offset=0, packed=False, diag=False, workspace=None,
-                              events=None, out=None):
+                              events=None, out=None, entropy=False, outcome=False, top_m=0):
     """Single-stage verify through a linear LM head W [V, d] (one d-vector per
     vocabulary entry): q from h_draft [B, k, d], p from h_target [B, k+1, d].
     Returns the same dict as spec_verify_single.  ``out`` reuses the output
@@ -301,7 +323,7 @@ def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperat
             out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
             out["cu_offsets"] = _int_out((B + 1,), dev)
     out["workspace"] = ws
-    dg = _make_diag(diag, events, B, k, dev, out)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m)
     _check(lib.spec_verify_lmhead_single(
         ctypes.byref(desc), d, _ptr(h_draft), _ptr(h_target), _ptr(w_vocab),
         _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
@@ -313,7 +335,7 @@ def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperat
 
 def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=None, *,
                      window=4, seed=0, offset=0, packed=False, diag=False, workspace=None,
-                     events=None):
+                     events=None, entropy=False, outcome=False, top_m=0):
     """HiSpec two-stage verify L_d -> L_i -> L_f.  Returns a dict of device
     tensors: accept_len_inter (a1), accept_len_final (a2), out_tokens,
     num_emitted, num_drop (+ packed / diag on request).  Asynchronous."""
@@ -336,7 +358,7 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
     if packed:
         out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
         out["cu_offsets"] = _int_out((B + 1,), dev)
-    dg = _make_diag(diag, events, B, k, dev, out)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m)
     _check(lib.spec_verify_hier(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
         _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len_inter"]),
@@ -349,7 +371,7 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
 def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
                               block_table, seq_lens, *, block_size, max_freed, window=4,
                               seed=0, offset=0, diag=False, workspace=None, events=None,
-                              out=None, _lazy=False):
+                              out=None, entropy=False, outcome=False, top_m=0, _lazy=False):
     """spec_verify_hier plus the paged-KV rollback of block_table / seq_lens
     (in place) in the same launches.  Returns the spec_verify_hier dict plus
     freed_blocks [B, max_freed] and num_freed [B].  ``out``: a dict returned
@@ -384,7 +406,7 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
         if tuple(out["out_tokens"].shape) != (B, k + 1) or \
                 tuple(out["freed_blocks"].shape) != (B, max_freed):
             raise ValueError("out buffers do not match this call's shapes")
-    dg = _make_diag(diag, events, B, k, dev, out)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m)
     fn = lib.spec_verify_hier_rollback_lazy if _lazy else lib.spec_verify_hier_rollback
     _check(fn(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),

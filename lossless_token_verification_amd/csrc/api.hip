@@ -29,6 +29,9 @@ struct Plan {
   size_t ws_bytes = 0;
   size_t seq_bytes = 0;   // per-sequence slice counters and stage-1 counts
   size_t tile_bytes = 0;  // draw tile sums of both stages
+  size_t part_bytes = 0;  // chunk partials
+  size_t tpart_bytes = 0; // entropy partials (one double per chunk partial)
+  size_t pair_bytes = 0;  // outcome-export partials, B * 2 * (k+1) * nc
   int nt = 0;             // draw tiles per row
   int ns = 0;             // slices (workgroups) per sequence
   int tps = 0;            // draw tiles per slice
@@ -79,8 +82,12 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   // two slice counters and the lazy final exit's stage-1 counts
   p->seq_bytes = (static_cast<size_t>(B) * 3 * sizeof(int32_t) + 255) / 256 * 256;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
-  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes +
-                static_cast<size_t>(p->rows_total) * p->nc * sizeof(sv::Partial);
+  const size_t n_part = static_cast<size_t>(p->rows_total) * p->nc;
+  p->part_bytes = (n_part * sizeof(sv::Partial) + 255) / 256 * 256;
+  p->tpart_bytes = (n_part * sizeof(double) + 255) / 256 * 256;
+  p->pair_bytes = static_cast<size_t>(B) * 2 * (k + 1) * p->nc * sizeof(sv::PairPart);
+  p->ws_bytes = sv::kFlagsBytes + p->seq_bytes + p->tile_bytes + p->part_bytes + p->tpart_bytes +
+                p->pair_bytes;
   return SV_OK;
 }
 
@@ -107,6 +114,11 @@ int32_t check_i32(const void* ptr, bool required, const char* name) {
   return SV_OK;
 }
 
+bool wants_outcome(const spec_verify_diag* d) {
+  return d && (d->accept_mass || d->residual_tokens || d->residual_mass);
+}
+bool wants_byproducts(const spec_verify_diag* d) { return d && (d->entropy || wants_outcome(d)); }
+
 int32_t check_diag(const spec_verify_diag* diag) {
   if (!diag) return SV_OK;
   if (diag->uniforms && !aligned_to(diag->uniforms, 4))
@@ -115,6 +127,17 @@ int32_t check_diag(const spec_verify_diag* diag) {
     return fail(SV_ERR_MISALIGNED, "diag.probs not 8-byte aligned");
   if (diag->draws && !aligned_to(diag->draws, 8))
     return fail(SV_ERR_MISALIGNED, "diag.draws not 8-byte aligned");
+  if (diag->entropy && !aligned_to(diag->entropy, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.entropy not 4-byte aligned");
+  if (diag->accept_mass && !aligned_to(diag->accept_mass, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.accept_mass not 4-byte aligned");
+  if (diag->residual_tokens && !aligned_to(diag->residual_tokens, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.residual_tokens not 4-byte aligned");
+  if (diag->residual_mass && !aligned_to(diag->residual_mass, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.residual_mass not 4-byte aligned");
+  if ((diag->residual_tokens || diag->residual_mass) &&
+      (diag->top_m < 1 || diag->top_m > SV_MAX_TOP_M))
+    return fail(SV_ERR_INVALID_ARG, "diag.top_m must be in [1, " + std::to_string(SV_MAX_TOP_M) + "]");
   return SV_OK;
 }
 
@@ -208,6 +231,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
   if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
   SV_TRY(check_diag(diag));
+  if (lazy && wants_byproducts(diag))
+    return fail(SV_ERR_UNSUPPORTED, "the lazy final exit does not stream every row: no by-products");
   SV_TRY(check_workspace(p, workspace, workspace_bytes));
   if (kv)
     SV_TRY(check_kv(desc->batch, kv->max_blocks, kv->block_size, kv->table, kv->lens, nullptr,
@@ -219,8 +244,11 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   int32_t* seqw = reinterpret_cast<int32_t*>(ws + sv::kFlagsBytes);
   float* tsum = reinterpret_cast<float*>(ws + sv::kFlagsBytes + p.seq_bytes);
-  sv::Partial* partials =
-      reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes + p.tile_bytes);
+  char* part_base = ws + sv::kFlagsBytes + p.seq_bytes + p.tile_bytes;
+  sv::Partial* partials = reinterpret_cast<sv::Partial*>(part_base);
+  double* tpart = reinterpret_cast<double*>(part_base + p.part_bytes);
+  sv::PairPart* pair = reinterpret_cast<sv::PairPart*>(part_base + p.part_bytes + p.tpart_bytes);
+  const bool want_entropy = diag && diag->entropy;
   const int B = desc->batch;
   hipError_t err;
 
@@ -240,6 +268,7 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.clear_words = seqw;   // slice counters
   sa.n_clear = 2 * B;
   sa.flags = flags;
+  sa.tpart = want_entropy ? tpart : nullptr;
   int32_t* lazy_a1 = lazy ? seqw + 2 * B : nullptr;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
@@ -324,6 +353,40 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     sv::PackArgs pa{desc->batch, desc->num_draft, out_tokens, num_emitted, packed, cu_offsets};
     err = sv::launch_pack(pa, st);
     if (err != hipSuccess) return device_error(err, "pack launch");
+  }
+
+  if (wants_byproducts(diag)) {
+    sv::ByArgs ba{};
+    ba.B = B;
+    ba.k = desc->num_draft;
+    ba.V = desc->vocab;
+    ba.dtype = desc->dtype;
+    ba.nc = p.nc;
+    ba.hier = num_exits == 3;
+    ba.ld = p.ld;
+    for (int e = 0; e < 3; ++e) {
+      ba.exit_ptr[e] = e < num_exits ? logits[e] : nullptr;
+      ba.exit_pos[e] = p.exit_pos[e];
+      ba.exit_row0[e] = e < num_exits ? p.exit_row0[e] : INT32_MAX;
+    }
+    ba.partials = partials;
+    ba.tpart = tpart;
+    ba.temperature = temperature;
+    ba.rows = static_cast<int32_t>(p.rows_total);
+    ba.entropy = diag->entropy;
+    ba.pair = pair;
+    ba.beta = diag->accept_mass;
+    ba.top_tok = diag->residual_tokens;
+    ba.top_mass = diag->residual_mass;
+    ba.top_m = (diag->residual_tokens || diag->residual_mass) ? diag->top_m : 0;
+    if (want_entropy && p.rows_total > 0) {
+      err = sv::launch_entropy(ba, st);
+      if (err != hipSuccess) return device_error(err, "entropy launch");
+    }
+    if (wants_outcome(diag)) {
+      err = sv::launch_outcome(ba, st);
+      if (err != hipSuccess) return device_error(err, "outcome export launch");
+    }
   }
   return SV_OK;
 }
@@ -410,6 +473,8 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
   SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
   if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
   SV_TRY(check_diag(diag));
+  if (wants_byproducts(diag))
+    return fail(SV_ERR_UNSUPPORTED, "the LM-head path stores no logit rows: no by-products");
   if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned_to(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < p.ws_bytes)

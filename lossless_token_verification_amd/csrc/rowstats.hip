@@ -2,14 +2,15 @@
 // logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk) of
 // the launch's rows; the first workgroups also clear the slice counters of the
 // verification that follows on the same stream.  With a lazy final exit, the
-// L_f rows past each sequence's stage-1 stop are skipped.
+// L_f rows past each sequence's stage-1 stop are skipped.  The ENT variant
+// (row entropies requested) also writes each chunk's T.
 #include "sv_stats.h"
 
 namespace sv {
 
 namespace {
 
-template <int DT>
+template <int DT, bool ENT>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   constexpr int ES = DT == 1 ? 2 : 4;
   constexpr int CE = kChunkBytes / ES;
@@ -34,18 +35,28 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   const float s = greedy ? 0.0f : kLog2e / tau;
   const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
   const int e0 = chunk * CE;
-  const Partial p = chunk_stats<DT>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds);
-  if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
+  double T;
+  const Partial p = chunk_stats<DT, ENT>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+  if (tid == 0) {
+    a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
+    if constexpr (ENT) a.tpart[static_cast<int64_t>(row) * a.nc + chunk] = T;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(rows_total * a.nc));
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(rowstats_kernel<1>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(rowstats_kernel<0>, grid, dim3(kThreads), 0, st, a);
+  if (a.tpart) {
+    if (a.dtype == 1)
+      hipLaunchKernelGGL((rowstats_kernel<1, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((rowstats_kernel<0, true>), grid, dim3(kThreads), 0, st, a);
+  } else if (a.dtype == 1) {
+    hipLaunchKernelGGL((rowstats_kernel<1, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((rowstats_kernel<0, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -135,6 +135,39 @@ hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st);
 hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 
+// By-products of a verification call: the entropy of every streamed row
+// (from the chunk partials and their T), and per tested position the
+// acceptance mass beta = sum min(p, q) with the largest entries of the
+// residual max(0, p - q).  The outcome export is one pass over the rows of
+// every position (each workgroup one 64 KiB chunk of q, p and, for the
+// hierarchy, L_f) writing a PairPart per (sequence, stage, position, chunk),
+// then one wavefront per (sequence, stage, position) merging them.
+constexpr int kTopM = 8;       // residual tokens one position can export
+struct PairPart {
+  double beta;                 // sum over the chunk of min(p, q)
+  float mass[kTopM];           // the chunk's largest residuals, largest first
+  int32_t tok[kTopM];          // their tokens (-1: none)
+};
+static_assert(sizeof(PairPart) == 72, "PairPart layout");
+struct ByArgs {
+  int32_t B, k, V, dtype, nc, hier;
+  int64_t ld;
+  const void* exit_ptr[3];
+  int32_t exit_pos[3], exit_row0[3];
+  const Partial* partials;
+  const double* tpart;         // entropy partials or NULL
+  const float* temperature;
+  int32_t rows;                // rows of every exit
+  float* entropy;              // [rows] or NULL
+  PairPart* pair;              // [B, 2, k+1, nc] workspace
+  float* beta;                 // [B, 2, k+1] or NULL
+  int32_t* top_tok;            // [B, 2, k+1, top_m] or NULL
+  float* top_mass;             // [B, 2, k+1, top_m] or NULL
+  int32_t top_m;
+};
+hipError_t launch_entropy(const ByArgs& a, hipStream_t st);
+hipError_t launch_outcome(const ByArgs& a, hipStream_t st);
+
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_kv_truncate(const KvArgs& a, hipStream_t st);

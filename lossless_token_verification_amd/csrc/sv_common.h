@@ -53,6 +53,9 @@ struct StatsArgs {
   // Lazy final exit: skip L_f row j of sequence b when j > a1[b] (stage 1
   // stopped before it, so stage 2 never reads it); NULL: every row.
   const int32_t* lazy_a1;
+  // Row entropies requested: per (row, chunk) T = sum 2^(l*s - c) * (l*s - c)
+  // beside the partial (same reference c); NULL: not computed.
+  double* tpart;
 };
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);

@@ -7,6 +7,9 @@
 //   temperature > 0: c = round(max * s) and S = sum 2^(l * s - c), with
 //                    s = log2(e) / temperature (fp32 exponent, fp64 sum);
 //   temperature = 0: the maximum and its lowest index (greedy decoding).
+// With ENT the sampled rows also give T = sum 2^(l * s - c) * (l * s - c),
+// which turns the row's merged (c, S, T) into its entropy ln S - ln 2 * T / S
+// at the cost of one multiply-add per element.
 // The softmax of a row is the token distribution of that exit at that position
 // (HiSpec summary, section 2 "Kernmechanismus": L_d, L_i and L_f each yield a
 // token distribution).
@@ -20,6 +23,7 @@ struct Red {
   float key;
   int idx;
   double S;
+  double T;
 };
 
 // Workgroup reduction of greedy (max, lowest index) pairs.
@@ -72,6 +76,44 @@ __device__ inline void block_logsum(float& c, double& S, Red* lds) {
   c = cm;
 }
 
+// The same reduction carrying T: moving a partial from reference c_t to cm
+// shifts every exponent by c_t - cm, so T becomes 2^(c_t - cm) * (T + (c_t - cm) * S).
+__device__ inline void block_logsum_t(float& c, double& S, double& T, Red* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  float cm = wave_max(c);
+  if (lane == 0) lds[wave].key = cm;
+  __syncthreads();
+  cm = lds[0].key;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) cm = fmaxf(cm, lds[w].key);
+  double Sr = 0.0, Tr = 0.0;
+  if (S > 0.0) {
+    const double d = static_cast<double>(c) - static_cast<double>(cm);
+    const double f = exp2(d);
+    Sr = S * f;
+    Tr = (T + d * S) * f;
+  }
+  Sr = wave_sum(Sr);
+  Tr = wave_sum(Tr);
+  __syncthreads();
+  if (lane == 0) {
+    lds[wave].S = Sr;
+    lds[wave].T = Tr;
+  }
+  __syncthreads();
+  S = lds[0].S;
+  T = lds[0].T;
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    S += lds[w].S;
+    T += lds[w].T;
+  }
+  c = cm;
+}
+
+// Exponent times weight for T; a weight of 0 (l = -inf included) adds 0.
+__device__ __forceinline__ float xlogw(float t, float y) { return t * fmaxf(y, -1e30f); }
+
 template <int DT>
 __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 4]) {
   if constexpr (DT == 1) {
@@ -86,14 +128,16 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 
 }
 
 // Partial statistics of elements [e0, e1) of one row (e1 - e0 <= one chunk).
-// Called by the whole workgroup (it contains barriers).
-template <int DT>
-__device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds) {
+// Called by the whole workgroup (it contains barriers).  With ENT, T_out
+// receives the chunk's T (0 for a greedy row).
+template <int DT, bool ENT>
+__device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds,
+                               double& T_out) {
   constexpr int VPE = DT == 1 ? 8 : 4;
   const int tid = threadIdx.x;
   float m = -INFINITY;
   int idx = 0x7fffffff;
-  double S = 0.0;
+  double S = 0.0, T = 0.0;
   float c = -INFINITY;
 
   if ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0) {
@@ -145,16 +189,27 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
         float x[VPE];
         unpack<DT>(buf[i], x);
         float t[VPE];
+        float ty = 0.0f;
 #pragma unroll
-        for (int q = 0; q < VPE; ++q) t[q] = __builtin_amdgcn_exp2f(fmaf(x[q], s, nc_));
+        for (int q = 0; q < VPE; ++q) {
+          const float y = fmaf(x[q], s, nc_);
+          t[q] = __builtin_amdgcn_exp2f(y);
+          if constexpr (ENT) ty = fmaf(t[q], fmaxf(y, -1e30f), ty);
+        }
         // pairwise within the vector, fp64 across vectors
 #pragma unroll
         for (int w = VPE / 2; w > 0; w >>= 1)
 #pragma unroll
           for (int q = 0; q < w; ++q) t[q] += t[q + w];
         S += static_cast<double>(t[0]);
+        if constexpr (ENT) T += static_cast<double>(ty);
       }
-      if (has_tail) S += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xt, s, nc_)));
+      if (has_tail) {
+        const float y = fmaf(xt, s, nc_);
+        const float t = __builtin_amdgcn_exp2f(y);
+        S += static_cast<double>(t);
+        if constexpr (ENT) T += static_cast<double>(xlogw(t, y));
+      }
     }
   } else {
     // Misaligned row: scalar loads, two passes over the chunk.
@@ -167,21 +222,28 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
     }
     if (!greedy && m > -INFINITY) {
       c = m * s;
-      float acc = 0.0f;
+      float acc = 0.0f, acct = 0.0f;
       int n = 0;
       for (int i = e0 + tid; i < e1; i += kThreads) {
-        acc += __builtin_amdgcn_exp2f(fmaf(load_elem(rowp, i, DT), s, -c));
+        const float y = fmaf(load_elem(rowp, i, DT), s, -c);
+        const float t = __builtin_amdgcn_exp2f(y);
+        acc += t;
+        if constexpr (ENT) acct += xlogw(t, y);
         if (++n == 8) {
           S += static_cast<double>(acc);
+          if constexpr (ENT) T += static_cast<double>(acct);
           acc = 0.0f;
+          acct = 0.0f;
           n = 0;
         }
       }
       S += static_cast<double>(acc);
+      if constexpr (ENT) T += static_cast<double>(acct);
     }
   }
 
   Partial out;
+  T_out = 0.0;
   if (greedy) {
     block_argmax(m, idx, lds);
     out.key = m;
@@ -189,7 +251,12 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
     out.S = 0.0;
   } else {
     if (!(S > 0.0)) c = -INFINITY;   // thread saw no element
-    block_logsum(c, S, lds);
+    if constexpr (ENT) {
+      block_logsum_t(c, S, T, lds);
+      T_out = T;
+    } else {
+      block_logsum(c, S, lds);
+    }
     out.key = c;
     out.amax = -1;
     out.S = S;

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(sv):
 
 def test_version_and_status_strings(sv):
     lib = sv.library()
-    assert sv.abi_version() == 1
+    assert sv.abi_version() == 2
     for code, name in ((0, b"SV_OK"), (1, b"SV_ERR_INVALID_ARG"), (2, b"SV_ERR_UNSUPPORTED"),
                        (3, b"SV_ERR_MISALIGNED"), (4, b"SV_ERR_WORKSPACE"), (5, b"SV_ERR_DEVICE"),
                        (99, b"SV_ERR_UNKNOWN")):
@@ -55,12 +55,16 @@ def test_workspace_size_formula(sv):
 
     def tiles(V, per):
         return -(-V // per)
+    def parts(rows, nc, B, k):
+        # chunk partials (16 B), entropy partials (8 B), outcome-export partials (72 B)
+        return pad(rows * nc * 16) + pad(rows * nc * 8) + B * 2 * (k + 1) * nc * 72
+
     assert sv.workspace_bytes(256, 8, 128256, 1, 3) == \
-        256 + pad(256 * 12) + pad(256 * 2 * tiles(128256, 512) * 4) + 256 * 26 * 4 * 16
+        256 + pad(256 * 12) + pad(256 * 2 * tiles(128256, 512) * 4) + parts(256 * 26, 4, 256, 8)
     assert sv.workspace_bytes(64, 4, 32000, 1, 2) == \
-        256 + pad(64 * 12) + pad(64 * 2 * tiles(32000, 512) * 4) + 64 * 9 * 1 * 16
+        256 + pad(64 * 12) + pad(64 * 2 * tiles(32000, 512) * 4) + parts(64 * 9, 1, 64, 4)
     assert sv.workspace_bytes(32, 5, 151936, 0, 2) == \
-        256 + pad(32 * 12) + pad(32 * 2 * tiles(151936, 256) * 4) + 32 * 11 * 10 * 16
+        256 + pad(32 * 12) + pad(32 * 2 * tiles(151936, 256) * 4) + parts(32 * 11, 10, 32, 5)
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 
@@ -155,3 +159,40 @@ def test_lmhead_workspace_formula_and_checks(sv):
     assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *ptrs, *rest,
                                          ctypes.c_void_p(0x10000), 1 << 30, None,
                                          None) == sv.SV_ERR_MISALIGNED
+
+
+def test_byproduct_host_checks_without_gpu(sv):
+    """By-product requests are validated before any launch: top_m range, output
+    alignment, and the calls that cannot produce them (lazy final exit, LM head)."""
+    lib = sv.library()
+    d = sv.make_desc(2, 3, 100, 0)
+    p = ctypes.c_void_p(0x1000)
+    single = [p] * 10 + [ctypes.c_void_p(0x10000), 1 << 30]
+
+    dg = sv.Diag()
+    dg.residual_tokens = 0x2000
+    dg.top_m = 0
+    assert lib.spec_verify_single(ctypes.byref(d), *single, ctypes.byref(dg), None) == \
+        sv.SV_ERR_INVALID_ARG
+    assert b"top_m" in lib.spec_verify_last_error()
+    dg.top_m = sv.MAX_TOP_M + 1
+    assert lib.spec_verify_single(ctypes.byref(d), *single, ctypes.byref(dg), None) == \
+        sv.SV_ERR_INVALID_ARG
+
+    dg = sv.Diag()
+    dg.entropy = 0x2002
+    assert lib.spec_verify_single(ctypes.byref(d), *single, ctypes.byref(dg), None) == \
+        sv.SV_ERR_MISALIGNED
+
+    dg = sv.Diag()
+    dg.entropy = 0x2000
+    hier = [p] * 10 + [4, 16, p, p, p, 1, p, ctypes.c_void_p(0x10000), 1 << 30]
+    assert lib.spec_verify_hier_rollback_lazy(ctypes.byref(d), 4, *hier, ctypes.byref(dg),
+                                              None) == sv.SV_ERR_UNSUPPORTED
+    assert b"lazy" in lib.spec_verify_last_error()
+    dg = sv.Diag()
+    dg.accept_mass = 0x2000
+    db = sv.make_desc(2, 3, 100, 1)
+    lm = [ctypes.c_void_p(0x1000)] * 11 + [ctypes.c_void_p(0x10000), 1 << 30]
+    assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *lm, ctypes.byref(dg), None) == \
+        sv.SV_ERR_UNSUPPORTED

@@ -46,7 +46,7 @@ HIER_KEYS = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted"
 
 
 def test_library_is_the_hip_build(sv):
-    assert sv.abi_version() == 1
+    assert sv.abi_version() == 2
     assert sv._lib is not None and sv.LIB_PATH.endswith("libspecverify.so")
 
 
