@@ -37,6 +37,9 @@ lmhead     logits of a linear LM head (hidden . W^T, float64) fed to the
            single-stage verify.
 byproducts row entropies and the verification-outcome export (acceptance
            probability and largest residual tokens per tested position).
+tentative  cross-call tentative buffering: intermediate rounds append to a
+           per-sequence pending state, a flush verifies it against the final
+           exit.
 
 Parity status: every function here is pinned by a CPU test (tests/test_oracle_*)
 except the 4x32 *constants* of Philox, which no library in the CPU container
@@ -44,4 +47,4 @@ exposes; their round structure is pinned through the 4x64 instantiation
 against ``numpy.random.Philox`` and the constants are the published ones.
 """
 
-from . import philox, numerics, rule, verify, blocktable, byproducts  # noqa: F401
+from . import philox, numerics, rule, verify, blocktable, byproducts, tentative  # noqa: F401
