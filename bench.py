@@ -272,6 +272,63 @@ def bench_lmhead(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_tentative(args):
+    """The hierarchy across calls on the hierarchical workload: per step one
+    intermediate round (stage 1 on L_d, L_i; the output and its L_i rows
+    appended to the pending state) and one flush of every sequence's pending
+    tokens against the final exit (min_pending 1), i.e. the one-call
+    hierarchy split at the call boundary."""
+    import torch
+    import lossless_token_verification_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make("hier", 0, device=dev)
+    B, k, V = w["B"], w["k"], w["V"]
+    cap = k + 1
+    lf = torch.zeros((B, cap + 1, V), dtype=torch.bfloat16, device=dev)
+    lf[:, :k + 1] = w["lf_logits"]
+    pend = sv.make_pending(B, cap, V, torch.bfloat16, dev)
+    ws = sv.alloc_workspace(sv.tentative_workspace_bytes(B, k, V, torch.bfloat16, cap), dev)
+    print("[bench] tentative workload ready", file=sys.stderr, flush=True)
+
+    def step(i):
+        sv.spec_verify_tentative_round(w["ld_logits"], w["li_logits"], w["draft_tokens"],
+                                       w["temperature"], pend, seed=0, offset=2 * i,
+                                       workspace=ws)
+        return sv.spec_verify_tentative_flush(lf, w["temperature"], pend, min_pending=1,
+                                              seed=0, offset=2 * i, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev.hip.hipEventRecord(ev.ev[0], stream)
+    for i in range(args.steps):
+        out = step(1000 + i)
+    ev.hip.hipEventRecord(ev.ev[1], stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / args.steps
+    ev.close()
+    n = out["num_emitted"].cpu()
+    rows_read = B * k + B * (k + 1) + 2 * int(n.clamp(min=1).sum())
+    line = {
+        "metric": "verified draft tokens/s, hierarchy across calls (round + flush), "
+                  "B=256 k=8 V=128256 bf16",
+        "value": round(B * k / (ms / 1e3), 1), "unit": "verified draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "hierarchical workload; one intermediate round, then a flush "
+                               "of the pending tokens against the final exit",
+                   "B": B, "k": k, "V": V, "capacity": cap},
+        "approx_rows_read_per_step": rows_read,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,10 +342,12 @@ def main():
                     help="also run a copy of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into the traffic file and exit")
-    ap.add_argument("--path", choices=("hier", "hier_lazy", "lmhead"), default="hier",
+    ap.add_argument("--path", choices=("hier", "hier_lazy", "lmhead", "tentative"),
+                    default="hier",
                     help="hier: the hierarchical verify + rollback step (default); hier_lazy: "
                          "the same step reading only the L_f rows stage 2 can reach; lmhead: "
-                         "the fused LM-head verify")
+                         "the fused LM-head verify; tentative: the hierarchy across calls, "
+                         "one intermediate round then a flush of the pending tokens")
     ap.add_argument("--byproducts", choices=("none", "entropy", "outcome", "all"), default="none",
                     help="hier path only: also compute the row entropies, the outcome export "
                          "(acceptance mass and the 8 largest residual tokens per position), "
@@ -305,6 +364,9 @@ def main():
 
     if args.path == "lmhead":
         bench_lmhead(args)
+        return
+    if args.path == "tentative":
+        bench_tentative(args)
         return
 
     cpu = None

@@ -103,6 +103,7 @@ extern "C" {
 /* Device flags (spec_verify_device_status). */
 #define SV_FLAG_TOKEN_RANGE 1u /* a drafted token outside [0, V) was rejected        */
 #define SV_FLAG_TEMPERATURE 2u /* a negative or NaN temperature was treated as 0    */
+#define SV_FLAG_PENDING_FULL 4u /* a round's output did not fit the pending capacity */
 
 typedef struct {
   int32_t batch;      /* B >= 0 sequences (0: nothing to do)                  */
@@ -325,6 +326,75 @@ int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t win
                                        int32_t* num_freed, void* workspace,
                                        size_t workspace_bytes, const spec_verify_diag* diag,
                                        void* hip_stream);
+
+/* Pending tentative tokens of every sequence, carried across calls (caller-
+ * owned device memory, zero the counts before the first round).  HiSpec
+ * accumulates tentatively accepted tokens, N_i = 4 by default, before the
+ * full model verifies them (HiSpec summary, section 2, bullet "Dynamische
+ * Verifizierungsrichtlinie"): a round runs the intermediate verification
+ * L_d -> L_i and appends its output to this state, a flush verifies the state
+ * against the final exit L_f. */
+typedef struct {
+  int32_t* count;    /* [B] pending tokens per sequence, 0..capacity             */
+  int32_t* tokens;   /* [B, capacity] the pending tokens, in order              */
+  void* rows;        /* [B, capacity, row_stride] logits of the desc's dtype: the
+                        L_i row each pending token was accepted or drawn under */
+  int32_t capacity;  /* 1..SV_MAX_DRAFT                                          */
+} spec_verify_pending;
+
+/* Workspace bytes of spec_verify_tentative_round and _flush for this desc
+ * (num_draft = drafts per round) and capacity; 0 if either is invalid. */
+size_t spec_verify_tentative_workspace_bytes(const spec_verify_desc* desc, int32_t capacity);
+
+/* One intermediate verification round: stage 1 of the hierarchy (the standard
+ * rule, q = L_d, p = L_i, Philox stage 0) for every sequence, then, for every
+ * active sequence, its output t = (x_0..x_{a1-1}, y) is appended to the
+ * pending tokens and the L_i rows 0..a1 to the pending rows.
+ *   desc         B, k = drafts of this round, V, dtype, row_stride (also the
+ *                pending rows' stride), seed, offset (use a fresh offset per
+ *                call: the Philox counter is (j, b, stage, offset))
+ *   ld_logits    [B, k, V], li_logits [B, k+1, V], draft_tokens [B, k],
+ *   temperature  as for spec_verify_hier
+ *   active       [B] int32 device, 0 = leave this sequence's state alone; NULL
+ *                = every sequence
+ *   pending      the state (appended in place)
+ *   accept_len   [B] out: a1 of every sequence (active or not)
+ *   num_drop     [B] out or NULL: k - a1, the drafts discarded by this round
+ *                (their KV entries in the layers up to L_i are stale)
+ * A sequence whose output does not fit its remaining capacity gets what fits
+ * and sets SV_FLAG_PENDING_FULL.  Errors as for spec_verify_hier; capacity
+ * outside [1, SV_MAX_DRAFT] is SV_ERR_UNSUPPORTED. */
+int32_t spec_verify_tentative_round(const spec_verify_desc* desc, const void* ld_logits,
+                                    const void* li_logits, const int32_t* draft_tokens,
+                                    const float* temperature, const int32_t* active,
+                                    const spec_verify_pending* pending, int32_t* accept_len,
+                                    int32_t* num_drop, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream);
+
+/* Full verification of the pending tokens of every sequence holding at least
+ * max(1, min_pending) of them (the others are left alone): stage 2 of the
+ * hierarchy across calls -- the standard rule over t_0..t_{c-1} with q = the
+ * pending L_i rows and p = the final exit's rows, Philox stage 1 -- gives a2 =
+ * the first rejection (else c); on a rejection the correction z is drawn from
+ * norm(max(0, p - q)) at a2 and t_0..t_{a2-1}, z are emitted, otherwise all c
+ * pending tokens (no bonus, as in spec_verify_hier).  The flushed sequences'
+ * counts become 0.  Only the rows of pending positions are read.
+ *   desc         as for the rounds (num_draft is not used here)
+ *   lf_logits    [B, capacity+1, V] device: row j is the final exit's row at
+ *                pending position j (rows past the count are not read)
+ *   min_pending  the window N_i (>= 0)
+ *   accept_len   [B] out: a2, or -1 for a sequence not flushed
+ *   out_tokens   [B, capacity+1] out: emitted tokens, -1 padded
+ *   num_emitted  [B] out: 0 for a sequence not flushed
+ *   num_drop     [B] out or NULL: pending tokens discarded (c - a2 on a
+ *                rejection, else 0): their KV entries in every layer are stale
+ * A round followed by a flush with the same offset gives exactly the results
+ * of spec_verify_hier. */
+int32_t spec_verify_tentative_flush(const spec_verify_desc* desc, const void* lf_logits,
+                                    const float* temperature, int32_t min_pending,
+                                    const spec_verify_pending* pending, int32_t* accept_len,
+                                    int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Synchronises hip_stream, then copies the device flags (SV_FLAG_*) of the
  * last verify call that used `workspace` into *flags_out (host). */

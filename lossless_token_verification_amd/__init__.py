@@ -13,6 +13,9 @@ Functions mirror the C entry points:
 * ``spec_verify_hier``    -- HiSpec two-stage L_d -> L_i -> L_f verification;
 * ``kv_blocktable_truncate`` -- paged-KV rollback of rejected drafted slots;
 * ``spec_verify_hier_rollback`` -- the two above in the same launches;
+* ``spec_verify_tentative_round`` / ``spec_verify_tentative_flush`` -- the
+  hierarchy across calls: intermediate rounds append to a pending state
+  (``make_pending``), a flush verifies it against the final exit;
 * ``workspace_bytes``, ``validate``, ``device_status``, ``abi_version``.
 """
 
@@ -34,6 +37,7 @@ SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
 SV_FLAG_TOKEN_RANGE = 1
 SV_FLAG_TEMPERATURE = 2
+SV_FLAG_PENDING_FULL = 4
 MAX_DRAFT = 63
 MAX_VOCAB = 1 << 20
 MAX_HIDDEN = 1 << 16
@@ -46,6 +50,8 @@ EXPORTED = (
     "spec_verify_hier", "kv_blocktable_truncate", "spec_verify_hier_rollback",
     "spec_verify_device_status", "spec_verify_lmhead_workspace_bytes",
     "spec_verify_lmhead_single", "spec_verify_hier_rollback_lazy",
+    "spec_verify_tentative_workspace_bytes", "spec_verify_tentative_round",
+    "spec_verify_tentative_flush",
 )
 
 
@@ -62,6 +68,11 @@ class Diag(ctypes.Structure):
                 ("stats_end", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
                 ("accept_mass", ctypes.c_void_p), ("residual_tokens", ctypes.c_void_p),
                 ("residual_mass", ctypes.c_void_p), ("top_m", ctypes.c_int32)]
+
+
+class Pending(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("rows", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -113,6 +124,14 @@ def library():
     lib.spec_verify_lmhead_single.restype = i32
     lib.spec_verify_lmhead_single.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P, P, P,
                                               P, P, P, P, sz, ctypes.POINTER(Diag), P]
+    lib.spec_verify_tentative_workspace_bytes.restype = sz
+    lib.spec_verify_tentative_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i32]
+    lib.spec_verify_tentative_round.restype = i32
+    lib.spec_verify_tentative_round.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P,
+                                                ctypes.POINTER(Pending), P, P, P, sz, P]
+    lib.spec_verify_tentative_flush.restype = i32
+    lib.spec_verify_tentative_flush.argtypes = [ctypes.POINTER(Desc), P, P, i32,
+                                                ctypes.POINTER(Pending), P, P, P, P, P, sz, P]
     _lib = lib
     return lib
 
@@ -454,3 +473,98 @@ def device_status(workspace):
     _check(lib.spec_verify_device_status(_ptr(workspace), ctypes.byref(flags),
                                          _stream(workspace.device)))
     return int(flags.value)
+
+
+# --- cross-call tentative buffering ------------------------------------------
+
+def tentative_workspace_bytes(batch, num_draft, vocab, dtype, capacity, row_stride=0):
+    """Workspace bytes of the tentative round and flush calls."""
+    code = dtype if isinstance(dtype, int) else (SV_DTYPE_BF16 if dtype == torch.bfloat16
+                                                 else SV_DTYPE_F32)
+    d = make_desc(batch, num_draft, vocab, code, row_stride)
+    return int(library().spec_verify_tentative_workspace_bytes(ctypes.byref(d), int(capacity)))
+
+
+def make_pending(batch, capacity, vocab, dtype, device, row_stride=None):
+    """A zeroed pending state: count [B], tokens [B, capacity] int32 and the
+    pending L_i rows [B, capacity, row_stride] of ``dtype``."""
+    ld = vocab if row_stride is None else row_stride
+    return dict(count=torch.zeros((batch,), dtype=torch.int32, device=device),
+                tokens=torch.full((batch, capacity), -1, dtype=torch.int32, device=device),
+                rows=torch.zeros((batch, capacity, ld), dtype=dtype, device=device),
+                capacity=int(capacity))
+
+
+def _pending_struct(pending, B):
+    for name in ("count", "tokens", "rows"):
+        t = pending[name]
+        if not t.is_contiguous() or t.shape[0] != B:
+            raise ValueError(f"pending[{name!r}] must be contiguous with {B} sequences")
+    return Pending(pending["count"].data_ptr(), pending["tokens"].data_ptr(),
+                   pending["rows"].data_ptr(), int(pending["capacity"]))
+
+
+def spec_verify_tentative_round(ld_logits, li_logits, draft_tokens, temperature, pending, *,
+                                active=None, seed=0, offset=0, workspace=None):
+    """One intermediate verification round (stage 1, L_d -> L_i); every active
+    sequence's output and L_i rows are appended to ``pending`` (in place).
+    Returns dict(accept_len [B], num_drop [B], workspace).  Asynchronous."""
+    lib = library()
+    B, k, V = ld_logits.shape
+    dev = ld_logits.device
+    code = _dtype_code(ld_logits)
+    s0 = _logits(ld_logits, "ld_logits", B, k, ld_logits.dtype)
+    s1 = _logits(li_logits, "li_logits", B, k + 1, ld_logits.dtype)
+    if li_logits.shape[2] != V:
+        raise ValueError("exit vocabularies differ")
+    _prep_common(draft_tokens, temperature, B, k, dev)
+    rows = pending["rows"]
+    if rows.dtype != ld_logits.dtype or rows.dim() != 3 or rows.shape[1] != pending["capacity"]:
+        raise ValueError("pending rows must be [B, capacity, row_stride] of the logits' dtype")
+    ld = _common_stride([s0, s1, rows.shape[2]], V)
+    if active is not None and (active.dtype != torch.int32 or tuple(active.shape) != (B,)):
+        raise ValueError("active must be an int32 [B] device tensor")
+    desc = make_desc(B, k, V, code, ld, seed, offset)
+    need = lib.spec_verify_tentative_workspace_bytes(ctypes.byref(desc), int(pending["capacity"]))
+    ws = workspace if workspace is not None else alloc_workspace(need, dev)
+    out = dict(accept_len=_int_out((B,), dev), num_drop=_int_out((B,), dev), workspace=ws)
+    pd = _pending_struct(pending, B)
+    _check(lib.spec_verify_tentative_round(
+        ctypes.byref(desc), _ptr(ld_logits), _ptr(li_logits), _ptr(draft_tokens),
+        _ptr(temperature), _ptr(active), ctypes.byref(pd), _ptr(out["accept_len"]),
+        _ptr(out["num_drop"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def spec_verify_tentative_flush(lf_logits, temperature, pending, *, min_pending, seed=0,
+                                offset=0, workspace=None):
+    """Verify the pending tokens of every sequence holding at least
+    max(1, min_pending) of them against the final exit (lf_logits
+    [B, capacity+1, V]); the flushed sequences' counts become 0.  Returns
+    dict(accept_len (a2, -1 if not flushed), out_tokens [B, capacity+1],
+    num_emitted, num_drop, workspace).  Asynchronous."""
+    lib = library()
+    cap = int(pending["capacity"])
+    B, P, V = lf_logits.shape
+    dev = lf_logits.device
+    code = _dtype_code(lf_logits)
+    s = _logits(lf_logits, "lf_logits", B, cap + 1, lf_logits.dtype)
+    rows = pending["rows"]
+    if rows.dtype != lf_logits.dtype:
+        raise ValueError("pending rows and lf_logits differ in dtype")
+    if temperature is not None and (temperature.dtype != torch.float32 or
+                                    tuple(temperature.shape) != (B,) or
+                                    not temperature.is_contiguous() or temperature.device != dev):
+        raise ValueError("temperature must be a contiguous float32 [B] tensor on the logits' device")
+    ld = _common_stride([s, rows.shape[2]], V)
+    desc = make_desc(B, 1, V, code, ld, seed, offset)
+    need = lib.spec_verify_tentative_workspace_bytes(ctypes.byref(desc), cap)
+    ws = workspace if workspace is not None else alloc_workspace(need, dev)
+    out = dict(accept_len=_int_out((B,), dev), out_tokens=_int_out((B, cap + 1), dev),
+               num_emitted=_int_out((B,), dev), num_drop=_int_out((B,), dev), workspace=ws)
+    pd = _pending_struct(pending, B)
+    _check(lib.spec_verify_tentative_flush(
+        ctypes.byref(desc), _ptr(lf_logits), _ptr(temperature), int(min_pending),
+        ctypes.byref(pd), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+        _ptr(out["num_emitted"]), _ptr(out["num_drop"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out

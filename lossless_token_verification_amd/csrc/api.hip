@@ -293,6 +293,7 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     sf.row_begin = p.exit_row0[2];
     sf.n_clear = 0;
     sf.lazy_a1 = lazy_a1;
+    sf.lazy_exit = 2;
     err = sv::launch_stats(sf, p.rows_total - p.exit_row0[2], st);
     if (err != hipSuccess) return device_error(err, "final-exit statistics launch");
   }
@@ -594,6 +595,191 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
   return SV_OK;
 }
 
+// Cross-call tentative buffering: a round is the single-stage verification of
+// (L_d, L_i) followed by the append to the pending state; a flush streams the
+// pending rows and the final exit's rows of the pending positions, then runs
+// the verification kernel in flush mode.
+struct TentPlan {
+  Plan round, flush;           // flush: k = capacity
+  size_t round_extra = 0, flush_extra = 0, ws_bytes = 0;
+};
+
+int32_t make_tent_plan(const spec_verify_desc* d, int32_t capacity, TentPlan* t) {
+  SV_TRY(make_plan(d, 2, &t->round));
+  if (capacity < 1 || capacity > SV_MAX_DRAFT)
+    return fail(SV_ERR_UNSUPPORTED, "pending capacity must be in [1, " + std::to_string(SV_MAX_DRAFT) + "]");
+  spec_verify_desc f = *d;
+  f.num_draft = capacity;
+  SV_TRY(make_plan(&f, 2, &t->flush));
+  const size_t B = static_cast<size_t>(d->batch);
+  // round: stage-1 output tokens [B, k+1] and counts [B]; flush: limits [B]
+  t->round_extra = pad256(B * (d->num_draft + 1) * sizeof(int32_t)) + pad256(B * sizeof(int32_t));
+  t->flush_extra = pad256(B * sizeof(int32_t));
+  t->ws_bytes = std::max(pad256(t->round.ws_bytes) + t->round_extra,
+                         pad256(t->flush.ws_bytes) + t->flush_extra);
+  return SV_OK;
+}
+
+int32_t check_pending(const spec_verify_pending* pd, int32_t batch, int32_t dtype) {
+  if (!pd) return fail(SV_ERR_INVALID_ARG, "pending is NULL");
+  if (batch == 0) return SV_OK;
+  SV_TRY(check_i32(pd->count, true, "pending.count"));
+  SV_TRY(check_i32(pd->tokens, true, "pending.tokens"));
+  if (!pd->rows) return fail(SV_ERR_INVALID_ARG, "pending.rows is NULL");
+  if (!aligned_to(pd->rows, sv::elem_bytes(dtype)))
+    return fail(SV_ERR_MISALIGNED, "pending.rows not aligned to its element size");
+  return SV_OK;
+}
+
+int32_t run_round(const spec_verify_desc* desc, const void* ld, const void* li,
+                  const int32_t* tokens, const float* temperature, const int32_t* active,
+                  const spec_verify_pending* pending, int32_t* accept_len, int32_t* num_drop,
+                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!pending) return fail(SV_ERR_INVALID_ARG, "pending is NULL");
+  TentPlan t;
+  SV_TRY(make_tent_plan(desc, pending->capacity, &t));
+  SV_TRY(check_pending(pending, desc->batch, desc->dtype));
+  SV_TRY(check_i32(active, false, "active"));
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < t.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, needs " + std::to_string(t.ws_bytes));
+  char* ws = static_cast<char*>(workspace);
+  const size_t off = pad256(t.round.ws_bytes);
+  const int B = desc->batch, k = desc->num_draft;
+  int32_t* t_out = reinterpret_cast<int32_t*>(ws + off);
+  int32_t* n_out = reinterpret_cast<int32_t*>(ws + off + pad256(static_cast<size_t>(B) * (k + 1) * 4));
+  const void* logits[3] = {ld, li, nullptr};
+  SV_TRY(run_verify(desc, 2, 1, logits, tokens, temperature, accept_len, nullptr, t_out, n_out,
+                    num_drop, nullptr, nullptr, workspace, t.round.ws_bytes, nullptr, hip_stream));
+  if (B == 0) return SV_OK;
+  sv::PendArgs pa{};
+  pa.B = B;
+  pa.k = k;
+  pa.V = desc->vocab;
+  pa.dtype = desc->dtype;
+  pa.cap = pending->capacity;
+  pa.nch = t.round.nc;
+  pa.ld = t.round.ld;
+  pa.li = li;
+  pa.active = active;
+  pa.a1 = accept_len;
+  pa.t_out = t_out;
+  pa.count = pending->count;
+  pa.tokens = pending->tokens;
+  pa.rows = pending->rows;
+  pa.flags = reinterpret_cast<uint32_t*>(ws);
+  const hipError_t err = sv::launch_pending_append(pa, static_cast<hipStream_t>(hip_stream));
+  if (err != hipSuccess) return device_error(err, "pending append launch");
+  return SV_OK;
+}
+
+int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* temperature,
+                  int32_t min_pending, const spec_verify_pending* pending, int32_t* accept_len,
+                  int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop, void* workspace,
+                  size_t workspace_bytes, void* hip_stream) {
+  if (!pending) return fail(SV_ERR_INVALID_ARG, "pending is NULL");
+  TentPlan t;
+  SV_TRY(make_tent_plan(desc, pending->capacity, &t));
+  const Plan& p = t.flush;
+  const int B = desc->batch, cap = pending->capacity;
+  SV_TRY(check_pending(pending, B, desc->dtype));
+  if (min_pending < 0) return fail(SV_ERR_INVALID_ARG, "min_pending < 0");
+  SV_TRY(check_logits(lf, B * (cap + 1), desc->dtype, "lf_logits"));
+  if (temperature && !aligned_to(temperature, 4))
+    return fail(SV_ERR_MISALIGNED, "temperature not 4-byte aligned");
+  const bool any = B > 0;
+  SV_TRY(check_i32(accept_len, any, "accept_len"));
+  SV_TRY(check_i32(out_tokens, any, "out_tokens"));
+  SV_TRY(check_i32(num_emitted, any, "num_emitted"));
+  SV_TRY(check_i32(num_drop, false, "num_drop"));
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned_to(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < t.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, needs " + std::to_string(t.ws_bytes));
+  if (!any) return SV_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
+  int32_t* seqw = reinterpret_cast<int32_t*>(ws + sv::kFlagsBytes);
+  float* tsum = reinterpret_cast<float*>(ws + sv::kFlagsBytes + p.seq_bytes);
+  sv::Partial* partials =
+      reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes + p.tile_bytes);
+  int32_t* lim = reinterpret_cast<int32_t*>(ws + pad256(p.ws_bytes));
+  hipError_t err;
+
+  sv::PendArgs pa{};
+  pa.B = B;
+  pa.cap = cap;
+  pa.count = pending->count;
+  pa.min_pending = min_pending;
+  pa.lim = lim;
+  err = sv::launch_flush_prep(pa, st);
+  if (err != hipSuccess) return device_error(err, "flush prep launch");
+
+  const void* exits[2] = {pending->rows, lf};
+  sv::StatsArgs sa{};
+  for (int e = 0; e < 3; ++e) {
+    sa.exit_ptr[e] = e < 2 ? exits[e] : nullptr;
+    sa.exit_pos[e] = p.exit_pos[e];
+    sa.exit_row0[e] = e < 2 ? p.exit_row0[e] : INT32_MAX;
+  }
+  sa.num_exits = 2;
+  sa.V = desc->vocab;
+  sa.nc = p.nc;
+  sa.dtype = desc->dtype;
+  sa.ld = p.ld;
+  sa.temperature = temperature;
+  sa.partials = partials;
+  sa.clear_words = seqw;
+  sa.n_clear = 2 * B;
+  sa.flags = flags;
+  sa.lazy_a1 = lim;   // rows past each sequence's last pending position are not read
+  sa.lazy_exit = 0;
+  err = sv::launch_stats(sa, p.rows_total, st);
+  if (err != hipSuccess) return device_error(err, "row statistics launch");
+
+  sv::VerifyArgs va{};
+  va.hier = 0;
+  va.B = B;
+  va.k = cap;
+  va.V = desc->vocab;
+  va.dtype = desc->dtype;
+  va.nc = p.nc;
+  va.window = 1;
+  va.nt = p.nt;
+  va.ns = p.ns;
+  va.tps = p.tps;
+  va.ld = p.ld;
+  for (int e = 0; e < 3; ++e) {
+    va.exit_ptr[e] = e < 2 ? exits[e] : nullptr;
+    va.exit_row0[e] = e < 2 ? p.exit_row0[e] : 0;
+  }
+  va.partials = partials;
+  for (int s = 0; s < 2; ++s) {
+    va.tsum[s] = tsum + static_cast<size_t>(s) * B * p.nt;
+    va.cnt[s] = seqw + s * B;
+  }
+  va.tokens = pending->tokens;
+  va.temperature = temperature;
+  va.key0 = static_cast<uint32_t>(desc->seed & 0xffffffffu);
+  va.key1 = static_cast<uint32_t>(desc->seed >> 32);
+  va.offset = desc->offset;
+  va.accept_len = accept_len;
+  va.out_tokens = out_tokens;
+  va.num_emitted = num_emitted;
+  va.num_drop = num_drop;
+  va.flags = flags;
+  va.flush_lim = lim;
+  err = sv::launch_verify(va, st);
+  if (err != hipSuccess) return device_error(err, "flush verify launch");
+  err = sv::launch_flush_reset(pa, st);
+  if (err != hipSuccess) return device_error(err, "flush reset launch");
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -728,6 +914,33 @@ int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t win
   return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
                     accept_len_final, out_tokens, num_emitted, num_drop, nullptr, nullptr,
                     workspace, workspace_bytes, diag, hip_stream, &kv, true);
+}
+
+size_t spec_verify_tentative_workspace_bytes(const spec_verify_desc* desc, int32_t capacity) {
+  TentPlan t;
+  const std::string keep = g_last_error;
+  const int32_t s = make_tent_plan(desc, capacity, &t);
+  g_last_error = keep;
+  return s == SV_OK ? t.ws_bytes : 0;
+}
+
+int32_t spec_verify_tentative_round(const spec_verify_desc* desc, const void* ld_logits,
+                                    const void* li_logits, const int32_t* draft_tokens,
+                                    const float* temperature, const int32_t* active,
+                                    const spec_verify_pending* pending, int32_t* accept_len,
+                                    int32_t* num_drop, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
+  return run_round(desc, ld_logits, li_logits, draft_tokens, temperature, active, pending,
+                   accept_len, num_drop, workspace, workspace_bytes, hip_stream);
+}
+
+int32_t spec_verify_tentative_flush(const spec_verify_desc* desc, const void* lf_logits,
+                                    const float* temperature, int32_t min_pending,
+                                    const spec_verify_pending* pending, int32_t* accept_len,
+                                    int32_t* out_tokens, int32_t* num_emitted, int32_t* num_drop,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return run_flush(desc, lf_logits, temperature, min_pending, pending, accept_len, out_tokens,
+                   num_emitted, num_drop, workspace, workspace_bytes, hip_stream);
 }
 
 int32_t spec_verify_device_status(const void* workspace, uint32_t* flags_out, void* hip_stream) {

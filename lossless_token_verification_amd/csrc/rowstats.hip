@@ -1,8 +1,9 @@
 // The HBM stream: partial softmax statistics of every 64 KiB chunk of every
 // logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk) of
 // the launch's rows; the first workgroups also clear the slice counters of the
-// verification that follows on the same stream.  With a lazy final exit, the
-// L_f rows past each sequence's stage-1 stop are skipped.  The ENT variant
+// verification that follows on the same stream.  Rows no later step reads are
+// skipped: with a lazy final exit the L_f rows past each sequence's stage-1
+// stop, in a flush the rows past each sequence's last pending token.  The ENT variant
 // (row entropies requested) also writes each chunk's T.
 #include "sv_stats.h"
 
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
   const int local = row - a.exit_row0[e];
   const int b = local / a.exit_pos[e];
-  if (a.lazy_a1 && e == 2 && local - b * a.exit_pos[2] > a.lazy_a1[b]) return;
+  if (a.lazy_a1 && e >= a.lazy_exit && local - b * a.exit_pos[e] > a.lazy_a1[b]) return;
   const float tau = a.temperature ? a.temperature[b] : 1.0f;
   const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
   const float s = greedy ? 0.0f : kLog2e / tau;

@@ -63,6 +63,11 @@ struct VerifyArgs {
   // L_f rows 0..a1 (the only ones stage 2 reads).  NULL: every row.
   int32_t stage1_only;
   int32_t* lazy_a1;
+  // Flush of pending tentative tokens: a single-stage chain per sequence over
+  // its n = flush_lim[b] + 1 pending tokens (0: the sequence is not flushed),
+  // q = exit 0 (the pending L_i rows), p = exit 1 (the final exit), Philox
+  // stage 1, no bonus.  NULL: an ordinary verification.
+  const int32_t* flush_lim;
   // optional paged-KV rollback of every sequence once its result is known
   int32_t* kv_table;       // [B, kv_max_blocks] or NULL
   int32_t* kv_lens;        // [B]
@@ -165,6 +170,28 @@ struct ByArgs {
   float* top_mass;             // [B, 2, k+1, top_m] or NULL
   int32_t top_m;
 };
+// Pending tentative tokens across calls: a round appends each active
+// sequence's stage-1 output (a1 accepted drafts and y) and the L_i rows it was
+// tested or drawn under; a flush verifies them against the final exit.
+struct PendArgs {
+  int32_t B, k, V, dtype, cap, nch;   // nch: 64 KiB chunks per row
+  int64_t ld;
+  const void* li;            // [B, k+1, ld] L_i logits of the round
+  const int32_t* active;     // [B] or NULL (every sequence)
+  const int32_t* a1;         // [B] stage-1 accept counts
+  const int32_t* t_out;      // [B, k+1] stage-1 output tokens
+  int32_t* count;            // [B] pending tokens
+  int32_t* tokens;           // [B, cap]
+  void* rows;                // [B, cap, ld]
+  int32_t min_pending;       // flush threshold
+  int32_t* lim;              // [B] flush: last pending position, -1 = not flushed
+  uint32_t* flags;
+};
+constexpr uint32_t kFlagPendingFull = 4u;
+hipError_t launch_pending_append(const PendArgs& a, hipStream_t st);
+hipError_t launch_flush_prep(const PendArgs& a, hipStream_t st);
+hipError_t launch_flush_reset(const PendArgs& a, hipStream_t st);
+
 hipError_t launch_entropy(const ByArgs& a, hipStream_t st);
 hipError_t launch_outcome(const ByArgs& a, hipStream_t st);
 

@@ -50,9 +50,11 @@ struct StatsArgs {
   int32_t n_clear;
   uint32_t* flags;
   int32_t row_begin;       // first row of this launch (rows are launched in order)
-  // Lazy final exit: skip L_f row j of sequence b when j > a1[b] (stage 1
-  // stopped before it, so stage 2 never reads it); NULL: every row.
+  // Rows nobody reads: skip row j of sequence b in exits e >= lazy_exit when
+  // j > lazy_a1[b] (the lazy final exit: L_f rows past stage 1's stop; a
+  // flush of pending tokens: rows past the last pending one); NULL: every row.
   const int32_t* lazy_a1;
+  int32_t lazy_exit;
   // Row entropies requested: per (row, chunk) T = sum 2^(l*s - c) * (l*s - c)
   // beside the partial (same reference c); NULL: not computed.
   double* tpart;

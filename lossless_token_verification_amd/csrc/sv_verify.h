@@ -834,6 +834,23 @@ struct SeqCtx {
     }
   }
 
+  // Outputs of a flush of c pending tokens: t_0..t_{emitted_n-2} and last_tok,
+  // a2, and the pending tokens discarded (c - a2 on a rejection, else 0).
+  __device__ void write_flush(int c, int emitted_n, int last_tok, int a2) {
+    const int tid = threadIdx.x;
+    if (tid <= k) {
+      int t = -1;
+      if (tid < emitted_n - 1) t = sm.toks[tid];
+      else if (tid == emitted_n - 1) t = last_tok;
+      a.out_tokens[static_cast<int64_t>(b) * (k + 1) + tid] = t;
+    }
+    if (tid == 0) {
+      a.accept_len[b] = a2;
+      a.num_emitted[b] = emitted_n;
+      if (a.num_drop) a.num_drop[b] = a2 >= 0 && a2 < c ? c - a2 : 0;
+    }
+  }
+
   __device__ void write_outputs(int emitted_n, int last_tok, int a1, int a2) {
     const int tid = threadIdx.x;
     if (tid <= k) {
@@ -954,6 +971,30 @@ __device__ void verify_slice(const VerifyArgs& a, int b, int slice, VerifyShared
       float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
       d[0] = d[1] = NAN;
     }
+  }
+  if (a.flush_lim) {
+    // flush of pending tentative tokens (stage 2 of the hierarchy, across calls)
+    const int n = a.flush_lim[b] + 1;
+    if (n <= 0) {   // not flushed: nothing was streamed for this sequence
+      if (first) cx.write_flush(0, 0, -1, -1);
+      return;
+    }
+    cx.pregather(2);
+    cx.merge_all(n, n, 0);
+    const int a2 = cx.decide(0, 1, n, 1, false, n, first);
+    if (a2 == n) {   // every pending token accepted: no draw, no bonus
+      if (first) cx.write_flush(n, n, sm.toks[n - 1], a2);
+      return;
+    }
+    if (cx.greedy) {
+      if (first) cx.write_flush(n, a2 + 1, sm.st[1][a2].amax, a2);
+      return;
+    }
+    const int z = sliced_draw<DT>(cx, slice, 0, 1, a2, true, 0, sm.vs[a2], sm.st[1][a2],
+                                  sm.st[0][a2]);
+    if (z == -2) return;
+    cx.write_flush(n, a2 + 1, z, a2);
+    return;
   }
   if (a.stage1_only) {
     // lazy final exit, first pass: stage 1 alone, from L_d and L_i

@@ -1,0 +1,120 @@
+// Pending tentative tokens across calls (HiSpec summary, section 2, bullet
+// "Dynamische Verifizierungsrichtlinie": tentatively accepted tokens are
+// accumulated, N_i = 4 by default, before the full model verifies them; bullet
+// "Wiederverwendung von KV-Cache ...": entries of discarded tokens are dropped
+// before the next phase).
+//
+// A round appends each active sequence's stage-1 output -- the a1 accepted
+// drafts and the L_i correction or bonus y -- to its pending tokens, and the
+// L_i rows 0..a1 (the rows those tokens were accepted or drawn under, stage
+// 2's q) to its pending rows.  A flush verifies the pending tokens against the
+// final exit (the verification kernel's flush mode) and empties the state.
+#include "sv_args.h"
+
+namespace sv {
+
+namespace {
+
+// One workgroup per (sequence, position j <= a1, 64 KiB chunk): copies that
+// chunk of L_i row j to pending row count + j.  Rows that would not fit are
+// skipped (the count update flags them).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void append_rows_kernel(PendArgs a) {
+  constexpr int ES = DT == 1 ? 2 : 4;
+  constexpr int VPE = 16 / ES;
+  constexpr int CE = kChunkBytes / ES;
+  const int ch = blockIdx.x % a.nch;
+  const int rest = blockIdx.x / a.nch;
+  const int j = rest % (a.k + 1), b = rest / (a.k + 1);
+  if (a.active && !a.active[b]) return;
+  if (j > a.a1[b]) return;
+  const int dst = min(max(a.count[b], 0), a.cap) + j;
+  if (dst >= a.cap) return;
+  const char* src = static_cast<const char*>(a.li) + (static_cast<int64_t>(b) * (a.k + 1) + j) * a.ld * ES;
+  char* out = static_cast<char*>(a.rows) + (static_cast<int64_t>(b) * a.cap + dst) * a.ld * ES;
+  const int e0 = ch * CE, e1 = min(a.V, e0 + CE);
+  const int tid = threadIdx.x;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(out)) & 15) == 0) {
+    const int nfull = (e1 - e0) / VPE;
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src) + e0 / VPE;
+    u32x4* d4 = reinterpret_cast<u32x4*>(out) + e0 / VPE;
+    for (int v = tid; v < nfull; v += kThreads) d4[v] = __builtin_nontemporal_load(s4 + v);
+    for (int e = e0 + nfull * VPE + tid; e < e1; e += kThreads) {
+      if constexpr (DT == 1)
+        reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+      else
+        reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
+    }
+  } else {
+    for (int e = e0 + tid; e < e1; e += kThreads) {
+      if constexpr (DT == 1)
+        reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+      else
+        reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
+    }
+  }
+}
+
+// One thread per sequence: appends the a1 + 1 output tokens and advances the
+// count (after the row copies, which read the old count).
+__global__ __launch_bounds__(kThreads) void append_tokens_kernel(PendArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.B) return;
+  if (a.active && !a.active[b]) return;
+  const int c = min(max(a.count[b], 0), a.cap);
+  int n = a.a1[b] + 1;
+  const int room = a.cap - c;
+  if (n > room) {
+    atomicOr(a.flags, kFlagPendingFull);
+    n = room > 0 ? room : 0;
+  }
+  for (int i = 0; i < n; ++i)
+    a.tokens[static_cast<int64_t>(b) * a.cap + c + i] = a.t_out[static_cast<int64_t>(b) * (a.k + 1) + i];
+  a.count[b] = c + n;
+}
+
+// Flush bookkeeping, one thread per sequence.  prep: lim = last pending
+// position of a sequence with at least max(1, min_pending) pending tokens,
+// else -1.  reset: the flushed sequences' pending state empties.
+__global__ __launch_bounds__(kThreads) void flush_prep_kernel(PendArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.B) return;
+  const int c = min(max(a.count[b], 0), a.cap);
+  a.lim[b] = c >= max(1, a.min_pending) ? c - 1 : -1;
+}
+
+__global__ __launch_bounds__(kThreads) void flush_reset_kernel(PendArgs a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.B) return;
+  if (a.lim[b] >= 0) a.count[b] = 0;
+}
+
+unsigned blocks_for(int n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_pending_append(const PendArgs& a, hipStream_t st) {
+  const int64_t wg = static_cast<int64_t>(a.B) * (a.k + 1) * a.nch;
+  if (wg > 0) {
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(append_rows_kernel<1>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(append_rows_kernel<0>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(append_tokens_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flush_prep(const PendArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(flush_prep_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flush_reset(const PendArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(flush_reset_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

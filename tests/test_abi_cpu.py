@@ -31,7 +31,7 @@ def sv():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     assert set(names) == set(sv.EXPORTED)
     lib = ctypes.CDLL(sv.LIB_PATH)
     for n in names:
@@ -196,3 +196,43 @@ def test_byproduct_host_checks_without_gpu(sv):
     lm = [ctypes.c_void_p(0x1000)] * 11 + [ctypes.c_void_p(0x10000), 1 << 30]
     assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *lm, ctypes.byref(dg), None) == \
         sv.SV_ERR_UNSUPPORTED
+
+
+def test_tentative_host_checks_without_gpu(sv):
+    """Workspace sizing and the failures the tentative calls report before any
+    launch: capacity outside [1, 63], a missing pending state, a short
+    workspace."""
+    lib = sv.library()
+    B, k, V = 4, 3, 1000
+    d = sv.make_desc(B, k, V, 0)
+
+    def pad(n):
+        return (n + 255) // 256 * 256
+
+    cap = 10
+    rnd = sv.workspace_bytes(B, k, V, 0, 2)
+    fl = sv.workspace_bytes(B, cap, V, 0, 2)
+    want = max(pad(rnd) + pad(B * (k + 1) * 4) + pad(B * 4), pad(fl) + pad(B * 4))
+    assert sv.tentative_workspace_bytes(B, k, V, 0, cap) == want
+    assert sv.tentative_workspace_bytes(B, k, V, 0, 0) == 0
+    assert sv.tentative_workspace_bytes(B, k, V, 0, 64) == 0
+    p = ctypes.c_void_p(0x1000)
+    pend = sv.Pending(0x2000, 0x3000, 0x4000, 64)
+    args = [p] * 5
+    assert lib.spec_verify_tentative_round(ctypes.byref(d), *args, ctypes.byref(pend), p, p,
+                                           ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        sv.SV_ERR_UNSUPPORTED
+    assert lib.spec_verify_tentative_round(ctypes.byref(d), *args, None, p, p,
+                                           ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        sv.SV_ERR_INVALID_ARG
+    pend = sv.Pending(0x2000, 0x3000, 0x4000, cap)
+    assert lib.spec_verify_tentative_round(ctypes.byref(d), *args, ctypes.byref(pend), p, p,
+                                           ctypes.c_void_p(0x10000), 16, None) == \
+        sv.SV_ERR_WORKSPACE
+    assert lib.spec_verify_tentative_flush(ctypes.byref(d), p, None, -1, ctypes.byref(pend), p,
+                                           p, p, p, ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        sv.SV_ERR_INVALID_ARG
+    pend = sv.Pending(0x2000, 0x3000, 0x4002, cap)
+    assert lib.spec_verify_tentative_flush(ctypes.byref(d), p, None, 4, ctypes.byref(pend), p,
+                                           p, p, p, ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        sv.SV_ERR_MISALIGNED
