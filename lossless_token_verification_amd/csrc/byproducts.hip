@@ -128,30 +128,41 @@ struct TopList {
   __device__ __forceinline__ float dropped() const { return 0.0f; }
 };
 
+// Residuals and probabilities here are non-negative floats (or +0), whose
+// bit patterns order like unsigned integers: min and max run as integer
+// operations, exact and free of the float min/max NaN handling.
+__device__ __forceinline__ float umaxf(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+__device__ __forceinline__ float uminf(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+
 struct Top2 {
-  float v1, v2, drop;
+  uint32_t v1, v2, drop;   // float bits of non-negative values
   int32_t i1, i2;
   __device__ __forceinline__ void init() {
-    v1 = v2 = drop = 0.0f;
+    v1 = v2 = drop = 0u;
     i1 = i2 = -1;
   }
-  __device__ __forceinline__ void push(float r, int v) {
+  __device__ __forceinline__ void push(float rf, int v) {
+    const uint32_t r = __float_as_uint(rf);
     const bool g1 = r > v1, g2 = r > v2;
-    drop = fmaxf(drop, fminf(r, v2));   // the value that leaves (or never enters)
+    drop = max(drop, min(r, v2));   // the value that leaves (or never enters)
     i2 = g1 ? i1 : (g2 ? v : i2);
-    v2 = g1 ? v1 : (g2 ? r : v2);
+    v2 = max(v2, min(r, v1));
     i1 = g1 ? v : i1;
-    v1 = g1 ? r : v1;
+    v1 = max(v1, r);
   }
-  __device__ __forceinline__ float head_val() const { return v1; }
+  __device__ __forceinline__ float head_val() const { return __uint_as_float(v1); }
   __device__ __forceinline__ int head_idx() const { return i1; }
   __device__ __forceinline__ void pop() {
     v1 = v2;
     i1 = i2;
-    v2 = 0.0f;
+    v2 = 0u;
     i2 = -1;
   }
-  __device__ __forceinline__ float dropped() const { return drop; }
+  __device__ __forceinline__ float dropped() const { return __uint_as_float(drop); }
 };
 
 // (va, ia) ranks before (vb, ib): larger value, then lower index; empty
@@ -262,16 +273,19 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, bool h
   const float iq = sh.inv[0], ip = sh.inv[1], i_f = sh.inv[2];
   float b0 = 0.0f, b1 = 0.0f;
   auto visit = [&](float xq, float xp, float xf, int v) {
+    // no contraction: p - min(p, q) must see the same rounded p as the min,
+    // so that it is exactly 0 (never negative) where q >= p
+#pragma clang fp contract(off)
     const float pp = __builtin_amdgcn_exp2f(fmaf(xp, s, -cp)) * ip;
     if (has0) {
       const float pq = __builtin_amdgcn_exp2f(fmaf(xq, s, -cq)) * iq;
-      const float mn = fminf(pp, pq);
+      const float mn = uminf(pp, pq);
       b0 += mn;
       L0.push(pp - mn, v);
     }
     if (has1) {
       const float pf = __builtin_amdgcn_exp2f(fmaf(xf, s, -cf)) * i_f;
-      const float mn = fminf(pp, pf);
+      const float mn = uminf(pp, pf);
       b1 += mn;
       L1.push(pf - mn, v);
     }
