@@ -272,6 +272,66 @@ def bench_lmhead(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_single(args):
+    """The single-stage verify on one of the single-stage workloads.  Each call
+    is bracketed by its own HIP events; between calls a 1 GiB buffer is
+    written (outside the events), so that the logits are not served from the
+    256 MB memory-side cache ("cold"); a second pass without it gives the
+    warm figure.  Algorithmic bytes: every draft and target row read once."""
+    import torch
+    import lossless_token_verification_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make(args.workload, 0, device=dev)
+    B, k, V = w["B"], w["k"], w["V"]
+    es = 2 if w["dtype"] == "bf16" else 4
+    algo = B * (2 * k + 1) * V * es
+    ws = sv.alloc_workspace(sv.workspace_bytes(B, k, V, w["draft_logits"].dtype, 2), dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = HipEvents(2 * args.steps)
+    out = {}
+
+    def call(i):
+        return sv.spec_verify_single(w["draft_logits"], w["target_logits"], w["draft_tokens"],
+                                     w.get("temperature"), seed=0, offset=i, workspace=ws)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("cold", "warm"):
+        for i in range(args.steps):
+            if mode == "cold":
+                flush.fill_(float(i))
+            ev.hip.hipEventRecord(ev.ev[2 * i], stream)
+            call(i)
+            ev.hip.hipEventRecord(ev.ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        ts = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(args.steps))
+        res[mode] = dict(median_us=round(ts[len(ts) // 2], 2), p10_us=round(ts[len(ts) // 10], 2),
+                         p90_us=round(ts[(9 * len(ts)) // 10], 2))
+    ev.close()
+    us = res["cold"]["median_us"]
+    gbps = algo / (us * 1e-6) / 1e9
+    line = {
+        "metric": f"verified draft tokens/s, single-stage verify, {args.workload} workload",
+        "value": round(B * k / (us * 1e-6), 1), "unit": "verified draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "k": k, "V": V, "logits": w["dtype"]},
+        "per_call": res,
+        "roofline_call": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_call": algo,
+                          "t_roof_us": round(algo / (HBM_PEAK_GBPS * 1e9) * 1e6, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_tentative(args):
     """The hierarchy across calls on the hierarchical workload: per step one
     intermediate round (stage 1 on L_d, L_i; the output and its L_i rows
@@ -342,12 +402,15 @@ def main():
                     help="also run a copy of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into the traffic file and exit")
-    ap.add_argument("--path", choices=("hier", "hier_lazy", "lmhead", "tentative"),
+    ap.add_argument("--path", choices=("hier", "hier_lazy", "lmhead", "tentative", "single"),
                     default="hier",
                     help="hier: the hierarchical verify + rollback step (default); hier_lazy: "
                          "the same step reading only the L_f rows stage 2 can reach; lmhead: "
                          "the fused LM-head verify; tentative: the hierarchy across calls, "
-                         "one intermediate round then a flush of the pending tokens")
+                         "one intermediate round then a flush of the pending tokens; single: "
+                         "the single-stage verify on --workload")
+    ap.add_argument("--workload", choices=("tiny", "batched", "mixed_temp"), default="batched",
+                    help="single path only: the single-stage workload")
     ap.add_argument("--byproducts", choices=("none", "entropy", "outcome", "all"), default="none",
                     help="hier path only: also compute the row entropies, the outcome export "
                          "(acceptance mass and the 8 largest residual tokens per position), "
@@ -367,6 +430,9 @@ def main():
         return
     if args.path == "tentative":
         bench_tentative(args)
+        return
+    if args.path == "single":
+        bench_single(args)
         return
 
     cpu = None

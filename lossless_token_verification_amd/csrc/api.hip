@@ -76,7 +76,17 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   p->ld = ld;
   const int te = sv::tile_elems(d->dtype);
   p->nt = (d->vocab + te - 1) / te;
-  p->tps = num_exits == 3 ? sv::kTilesPerSliceJoint : sv::kTilesPerSlice;
+  // Draw tiles per slice: about kVerifyWorkgroups workgroups in the
+  // verification launch (small batches or short rows get more slices per
+  // sequence, so the draws still spread over the chip), between kMinTilesPerSlice
+  // and the most one slice's LDS staging takes (fewer for the hierarchy's
+  // three-row joint draw).
+  {
+    const int64_t cap = num_exits == 3 ? sv::kTilesPerSliceJoint : sv::kTilesPerSlice;
+    const int64_t want = (static_cast<int64_t>(p->nt) * B + sv::kVerifyWorkgroups - 1) /
+                         sv::kVerifyWorkgroups;
+    p->tps = static_cast<int>(std::min(cap, std::max<int64_t>(sv::kMinTilesPerSlice, want)));
+  }
   p->ns = (p->nt + p->tps - 1) / p->tps;
   if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
   // two slice counters and the lazy final exit's stage-1 counts

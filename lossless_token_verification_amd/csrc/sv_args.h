@@ -19,10 +19,13 @@ constexpr uint32_t kFlagTemperature = 2u;
 // [tile sums: 2 * B * nt floats] [partials: rows * nc], each area padded to
 // 256 B.
 constexpr size_t kFlagsBytes = 256;
-// Draw tiles each workgroup of a verification sums: two rows per tile for a
-// single draw, three for the hierarchy's joint draw of y and z.
+// Draw tiles each workgroup of a verification sums, at most: two rows per tile
+// for a single draw, three for the hierarchy's joint draw of y and z (the
+// plan takes fewer when that leaves the launch short of workgroups).
 constexpr int kTilesPerSlice = 128;
 constexpr int kTilesPerSliceJoint = 64;
+constexpr int kMinTilesPerSlice = 8;
+constexpr int64_t kVerifyWorkgroups = 1024;
 
 // The verification launches (stage 1 with its draw, stage-2 draw).
 struct VerifyArgs {
