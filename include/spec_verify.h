@@ -30,6 +30,15 @@
  * section 2, bullets "Wiederverwendung von KV-Cache ..." and "Unterstuetzung
  * fuer Batch-Inferenz").
  *
+ * spec_verify_tentative_round / _flush spread the same two stages over calls:
+ * rounds of intermediate verification append their tentatively accepted tokens
+ * to a caller-owned pending state until N_i are pending, then a flush verifies
+ * them against the final exit (HiSpec summary, section 2, bullet "Dynamische
+ * Verifizierungsrichtlinie").  On request the dense calls also return by-
+ * products of the same rows: the entropy of every row, and per tested position
+ * the acceptance probability and the likeliest correction tokens
+ * (spec_verify_diag).
+ *
  * Distributions are softmax(logits / temperature) per row, computed from the
  * logits inside the library; temperature 0 means greedy (one-hot at the
  * lowest-index maximum), which reduces the rule to an argmax prefix match.
