@@ -89,8 +89,10 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   }
   p->ns = (p->nt + p->tps - 1) / p->tps;
   if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
-  // two slice counters and the lazy final exit's stage-1 counts
-  p->seq_bytes = (static_cast<size_t>(B) * 3 * sizeof(int32_t) + 255) / 256 * 256;
+  // two slice counters, the lazy final exit's stage-1 counts, and its list of
+  // L_f rows to stream (a count, then up to B * (k + 1) row ids)
+  p->seq_bytes =
+      B > 0 ? ((static_cast<size_t>(B) * (3 + k + 1) + 1) * sizeof(int32_t) + 255) / 256 * 256 : 0;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
   const size_t n_part = static_cast<size_t>(p->rows_total) * p->nc;
   p->part_bytes = (n_part * sizeof(sv::Partial) + 255) / 256 * 256;
@@ -275,11 +277,13 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.ld = p.ld;
   sa.temperature = temperature;
   sa.partials = partials;
-  sa.clear_words = seqw;   // slice counters
-  sa.n_clear = 2 * B;
+  sa.clear_words = seqw;   // slice counters (and, lazy, the stage-1 counts and list count)
+  sa.n_clear = lazy ? 3 * B + 1 : 2 * B;
   sa.flags = flags;
   sa.tpart = want_entropy ? tpart : nullptr;
   int32_t* lazy_a1 = lazy ? seqw + 2 * B : nullptr;
+  int32_t* lf_count = seqw + 3 * B;       // lazy: L_f rows listed by stage 1
+  int32_t* lf_list = seqw + 3 * B + 1;
   if (diag && diag->stats_begin) {
     err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
     if (err != hipSuccess) return device_error(err, "event record");
@@ -297,14 +301,15 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
     va = stage1_args(desc, p, logits, partials, tokens, temperature, flags);
     va.stage1_only = 1;
     va.lazy_a1 = lazy_a1;
+    va.row_list_out = lf_list;
+    va.row_count_out = lf_count;
     err = sv::launch_verify(va, st);
     if (err != hipSuccess) return device_error(err, "stage-1 launch");
-    sv::StatsArgs sf = sa;
-    sf.row_begin = p.exit_row0[2];
+    sv::StatsArgs sf = sa;   // the listed L_f rows only
     sf.n_clear = 0;
-    sf.lazy_a1 = lazy_a1;
-    sf.lazy_exit = 2;
-    err = sv::launch_stats(sf, p.rows_total - p.exit_row0[2], st);
+    sf.row_list = lf_list;
+    sf.row_count = lf_count;
+    err = sv::launch_stats_list(sf, (p.rows_total - p.exit_row0[2]) * p.nc, st);
     if (err != hipSuccess) return device_error(err, "final-exit statistics launch");
   }
   if (diag && diag->stats_end) {
@@ -624,7 +629,8 @@ int32_t make_tent_plan(const spec_verify_desc* d, int32_t capacity, TentPlan* t)
   const size_t B = static_cast<size_t>(d->batch);
   // round: stage-1 output tokens [B, k+1] and counts [B]; flush: limits [B]
   t->round_extra = pad256(B * (d->num_draft + 1) * sizeof(int32_t)) + pad256(B * sizeof(int32_t));
-  t->flush_extra = pad256(B * sizeof(int32_t));
+  t->flush_extra = pad256(B * sizeof(int32_t)) +
+                   pad256((B * 2 * static_cast<size_t>(capacity) + 1) * sizeof(int32_t));
   t->ws_bytes = std::max(pad256(t->round.ws_bytes) + t->round_extra,
                          pad256(t->flush.ws_bytes) + t->flush_extra);
   return SV_OK;
@@ -718,6 +724,9 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
   sv::Partial* partials =
       reinterpret_cast<sv::Partial*>(ws + sv::kFlagsBytes + p.seq_bytes + p.tile_bytes);
   int32_t* lim = reinterpret_cast<int32_t*>(ws + pad256(p.ws_bytes));
+  int32_t* row_count = reinterpret_cast<int32_t*>(ws + pad256(p.ws_bytes) +
+                                                  pad256(static_cast<size_t>(B) * sizeof(int32_t)));
+  int32_t* row_list = row_count + 1;
   hipError_t err;
 
   sv::PendArgs pa{};
@@ -726,6 +735,10 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
   pa.count = pending->count;
   pa.min_pending = min_pending;
   pa.lim = lim;
+  pa.row0_q = p.exit_row0[0];
+  pa.row0_p = p.exit_row0[1];
+  pa.row_list = row_list;
+  pa.row_count = row_count;
   err = sv::launch_flush_prep(pa, st);
   if (err != hipSuccess) return device_error(err, "flush prep launch");
 
@@ -746,9 +759,9 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
   sa.clear_words = seqw;
   sa.n_clear = 2 * B;
   sa.flags = flags;
-  sa.lazy_a1 = lim;   // rows past each sequence's last pending position are not read
-  sa.lazy_exit = 0;
-  err = sv::launch_stats(sa, p.rows_total, st);
+  sa.row_list = row_list;   // the pending rows and L_f rows of the flushed sequences
+  sa.row_count = row_count;
+  err = sv::launch_stats_list(sa, p.rows_total * p.nc, st);
   if (err != hipSuccess) return device_error(err, "row statistics launch");
 
   sv::VerifyArgs va{};

@@ -1,10 +1,12 @@
 // The HBM stream: partial softmax statistics of every 64 KiB chunk of every
 // logit row of every exit (see sv_stats.h).  One workgroup per (row, chunk) of
 // the launch's rows; the first workgroups also clear the slice counters of the
-// verification that follows on the same stream.  Rows no later step reads are
-// skipped: with a lazy final exit the L_f rows past each sequence's stage-1
-// stop, in a flush the rows past each sequence's last pending token.  The ENT variant
-// (row entropies requested) also writes each chunk's T.
+// verification that follows on the same stream.  The ENT variant (row
+// entropies requested) also writes each chunk's T.  A row-list launch covers
+// only the rows an earlier launch listed (the lazy final exit's L_f rows up to
+// each stage-1 stop, a flush's pending rows and final-exit rows).
+#include <algorithm>
+
 #include "sv_stats.h"
 
 namespace sv {
@@ -30,7 +32,6 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
   const int local = row - a.exit_row0[e];
   const int b = local / a.exit_pos[e];
-  if (a.lazy_a1 && e >= a.lazy_exit && local - b * a.exit_pos[e] > a.lazy_a1[b]) return;
   const float tau = a.temperature ? a.temperature[b] : 1.0f;
   const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
   const float s = greedy ? 0.0f : kLog2e / tau;
@@ -44,7 +45,55 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   }
 }
 
+// Row-list mode: the workgroups loop over (listed row, chunk) items.  The
+// first workgroups clear the verification counters as above.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
+  constexpr int ES = DT == 1 ? 2 : 4;
+  constexpr int CE = kChunkBytes / ES;
+  __shared__ Red lds[kWaves];
+  const int tid = threadIdx.x;
+  {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
+    if (i < a.n_clear) a.clear_words[i] = 0;
+    if (i == 0) a.flags[0] = 0u;
+  }
+  const int n_items = *a.row_count * a.nc;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int rel = it / a.nc;
+    const int chunk = it - rel * a.nc;
+    const int row = a.row_list[rel];
+    int e = 0;
+    if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
+    if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
+    const int local = row - a.exit_row0[e];
+    const int b = local / a.exit_pos[e];
+    const float tau = a.temperature ? a.temperature[b] : 1.0f;
+    const bool greedy = !(tau > 0.0f) || !(tau < INFINITY);
+    const float s = greedy ? 0.0f : kLog2e / tau;
+    const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
+    const int e0 = chunk * CE;
+    double T;
+    const Partial p = chunk_stats<DT, false>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+    if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
+    __syncthreads();   // the next item reuses lds
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st) {
+  // two resident workgroups per CU (the looping kernel holds more registers)
+  constexpr int64_t kListWorkgroups = 512;
+  const int64_t clear_wg = (a.n_clear + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>(std::max<int64_t>(
+      1, std::max(clear_wg, std::min(max_items, kListWorkgroups)))));
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(rowstats_list_kernel<1>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(rowstats_list_kernel<0>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(rows_total * a.nc));

@@ -66,6 +66,10 @@ struct VerifyArgs {
   // L_f rows 0..a1 (the only ones stage 2 reads).  NULL: every row.
   int32_t stage1_only;
   int32_t* lazy_a1;
+  // ... and appends each sequence's L_f rows 0..a1 (global row ids) to
+  // row_list_out at an atomically advanced *row_count_out (NULL: no list)
+  int32_t* row_list_out;
+  int32_t* row_count_out;
   // Flush of pending tentative tokens: a single-stage chain per sequence over
   // its n = flush_lim[b] + 1 pending tokens (0: the sequence is not flushed),
   // q = exit 0 (the pending L_i rows), p = exit 1 (the final exit), Philox
@@ -188,6 +192,9 @@ struct PendArgs {
   void* rows;                // [B, cap, ld]
   int32_t min_pending;       // flush threshold
   int32_t* lim;              // [B] flush: last pending position, -1 = not flushed
+  int32_t row0_q, row0_p;    // flush: first global row of the pending rows and of L_f
+  int32_t* row_list;         // flush: the rows to stream (pending rows, then L_f rows,
+  int32_t* row_count;        //   of each flushed sequence in order) and their number
   uint32_t* flags;
 };
 constexpr uint32_t kFlagPendingFull = 4u;

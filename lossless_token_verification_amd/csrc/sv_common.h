@@ -50,17 +50,20 @@ struct StatsArgs {
   int32_t n_clear;
   uint32_t* flags;
   int32_t row_begin;       // first row of this launch (rows are launched in order)
-  // Rows nobody reads: skip row j of sequence b in exits e >= lazy_exit when
-  // j > lazy_a1[b] (the lazy final exit: L_f rows past stage 1's stop; a
-  // flush of pending tokens: rows past the last pending one); NULL: every row.
-  const int32_t* lazy_a1;
-  int32_t lazy_exit;
   // Row entropies requested: per (row, chunk) T = sum 2^(l*s - c) * (l*s - c)
   // beside the partial (same reference c); NULL: not computed.
   double* tpart;
+  // Row-list launch (launch_stats_list): the *row_count global row ids of
+  // row_list, written by an earlier launch.
+  const int32_t* row_list;
+  const int32_t* row_count;
 };
 
 hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);
+// The rows of a.row_list only: a grid of at most max_wg workgroups loops over
+// (listed row, chunk) items, so a launch costs the rows it reads rather than
+// one dispatched workgroup per possible row.
+hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // device helpers

@@ -1003,7 +1003,14 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
       cx.pregather(2);
       cx.merge_all(k, k + 1, 0);
       const int s1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1, false);
-      if (tid == 0) a.lazy_a1[b] = s1;
+      if (tid == 0) {
+        a.lazy_a1[b] = s1;
+        if (a.row_list_out) {   // the L_f rows stage 2 can read
+          const int base = atomicAdd(a.row_count_out, s1 + 1);
+          for (int j = 0; j <= s1; ++j)
+            a.row_list_out[base + j] = static_cast<int32_t>(cx.row_index(2, j));
+        }
+      }
       return;
     }
     cx.pregather(a.hier ? 3 : 2);

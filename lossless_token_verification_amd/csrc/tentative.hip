@@ -73,14 +73,41 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(PendArgs a) {
   a.count[b] = c + n;
 }
 
-// Flush bookkeeping, one thread per sequence.  prep: lim = last pending
-// position of a sequence with at least max(1, min_pending) pending tokens,
-// else -1.  reset: the flushed sequences' pending state empties.
+// Flush bookkeeping.  prep (one workgroup): lim = last pending position of a
+// sequence with at least max(1, min_pending) pending tokens, else -1, and the
+// list of rows the flush streams -- each flushed sequence's pending rows 0..c-1
+// then its L_f rows 0..c-1, sequences in order (a workgroup-wide exclusive scan
+// of 2c per batch of 256 sequences).  reset: the flushed sequences' pending
+// state empties.
 __global__ __launch_bounds__(kThreads) void flush_prep_kernel(PendArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.B) return;
-  const int c = min(max(a.count[b], 0), a.cap);
-  a.lim[b] = c >= max(1, a.min_pending) ? c - 1 : -1;
+  __shared__ int scan[kThreads];
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kThreads) {
+    const int b = b0 + tid;
+    int n = 0;
+    if (b < a.B) {
+      const int c = min(max(a.count[b], 0), a.cap);
+      n = c >= max(1, a.min_pending) ? c : 0;
+      a.lim[b] = n - 1;
+    }
+    scan[tid] = 2 * n;
+    __syncthreads();
+    for (int o = 1; o < kThreads; o <<= 1) {   // inclusive scan (Hillis-Steele)
+      const int v = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int off = base + scan[tid] - 2 * n;
+    for (int j = 0; j < n; ++j) {
+      a.row_list[off + j] = a.row0_q + b * a.cap + j;
+      a.row_list[off + n + j] = a.row0_p + b * (a.cap + 1) + j;
+    }
+    base += scan[kThreads - 1];
+    __syncthreads();   // scan[] is rewritten by the next batch
+  }
+  if (tid == 0) *a.row_count = base;
 }
 
 __global__ __launch_bounds__(kThreads) void flush_reset_kernel(PendArgs a) {
@@ -108,7 +135,7 @@ hipError_t launch_pending_append(const PendArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_flush_prep(const PendArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(flush_prep_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(flush_prep_kernel, dim3(1), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
