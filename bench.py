@@ -172,15 +172,21 @@ def traffic_from(fetch_dir, write_dir):
 
 # --- GPU --------------------------------------------------------------------
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+
 class HipEvents:
-    """Raw hipEvent_t handles (the library records them on its own stream)."""
+    """Raw hipEvent_t handles for timing only (the library has them take its
+    kernels' start and end times).  They carry no system-scope fence: nothing
+    waits on them for data."""
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            assert self.hip.hipEventCreateWithFlags(
+                ctypes.byref(e), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)) == 0
             self.ev.append(e)
 
     def elapsed_ms(self, a, b):
@@ -503,10 +509,17 @@ def main():
     ms_step = total_ms / args.steps
     k1_avg = sum(k1_ms) / len(k1_ms)
     if lazy:
-        # bytes actually read: every L_d and L_i row, L_f rows 0..a1 of each sequence
+        # bytes actually read: the L_d / L_i rows of the first N_i positions;
+        # L_f rows 0..a1 of a sequence that rejects a draft there; the rest of
+        # the L_d / L_i rows and every L_f row of one that accepts all N_i
         a1 = bufs["out"]["accept_len_inter"].cpu()
-        lf_rows = int((a1 + 1).sum())
-        read_bytes = (B * k + B * (k + 1) + lf_rows) * V * 2
+        r0 = min(max(w["window"], 1), k)
+        r1 = r0 + (1 if r0 == k else 0)
+        open_ = (a1 >= r0) if r0 < k else torch.zeros_like(a1, dtype=torch.bool)
+        n_open = int(open_.sum())
+        di_rows = B * (r0 + r1) + n_open * (2 * (k - r0) + 1)
+        lf_rows = int((a1 + 1)[~open_].sum()) + n_open * (k + 1)
+        read_bytes = (di_rows + lf_rows) * V * 2
         line = {
             "metric": "verified draft tokens/s, hierarchical verify with lazy final exit, "
                       "B=256 k=8 V=128256 bf16",
@@ -517,7 +530,8 @@ def main():
             "config": {"workload": "hierarchical verify + KV rollback, L_f rows read only up "
                                    "to each sequence's stage-1 stop", "B": B, "k": k, "V": V},
             "dense_bytes_per_step": launch_bytes, "read_bytes_per_step": read_bytes,
-            "lf_rows_read": lf_rows, "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
+            "ld_li_rows_read": di_rows, "lf_rows_read": lf_rows,
+            "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
             "stats_phase_us": round(k1_avg * 1e3, 2),
             "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         }

@@ -158,9 +158,13 @@ typedef struct {
   float* uniforms;   /* [B, 2, k+1, 2]: (u, v) of each position                   */
   double* probs;     /* [B, 2, k+1, 2]: (p(t_j), q(t_j)) of each tested position    */
   double* draws;     /* [B, 2, 4]: (R, v*R, C(y-1), C(y)) of each stage's draw      */
-  void* stats_begin; /* hipEvent_t recorded on hip_stream right before the
-                        row-statistics kernel (the HBM stream), or NULL          */
-  void* stats_end;   /* hipEvent_t recorded right after it, or NULL               */
+  void* stats_begin; /* hipEvent_t (created by the caller) that takes the start
+                        time of the row-statistics kernel (the HBM stream; the
+                        lazy call: its first statistics kernel), or NULL.  The
+                        kernel is launched with hipExtLaunchKernel, so the
+                        event adds no marker packet to hip_stream             */
+  void* stats_end;   /* hipEvent_t that takes its end time (the lazy call: the
+                        end of its last statistics kernel), or NULL          */
   float* entropy;    /* [rows of every exit]: row entropies, nats                */
   float* accept_mass;          /* [B, 2, k+1]: beta of each tested position      */
   int32_t* residual_tokens;    /* [B, 2, k+1, top_m]: largest residual tokens    */
@@ -319,10 +323,16 @@ int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
  * sequence's stage-1 stop are never read.  Stage 2 only tests tentative tokens
  * t_0..t_a1, so it reads L_f rows 0..a1 alone (HiSpec summary, section 2
  * "Kernmechanismus": the intermediate exit discards tokens early, before the
- * final exit verifies them).  The launches: statistics of every L_d and L_i
- * row, stage 1 per sequence, statistics of L_f rows 0..a1 only, then the
+ * final exit verifies them).  Stage 1 is streamed window by window in the
+ * same way: the L_d / L_i rows past the first `window` positions are read only
+ * for sequences that accepted every draft in that window.  The launches:
+ * statistics of the L_d and L_i rows of the first `window` positions; stage 1
+ * over them per sequence, which lists the rows still needed (L_f rows 0..a1
+ * where a draft was rejected in the window, otherwise the remaining L_d /
+ * L_i rows and every L_f row); statistics of the listed rows; then the
  * verification.  Results are bit-identical to spec_verify_hier_rollback's;
- * the bytes read depend on the data.  Same arguments and workspace. */
+ * the bytes read depend on the data.  Same arguments and workspace; the
+ * by-product fields of diag are rejected (SV_ERR_UNSUPPORTED). */
 int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t window,
                                        const void* ld_logits, const void* li_logits,
                                        const void* lf_logits, const int32_t* draft_tokens,

@@ -89,10 +89,13 @@ int32_t make_plan(const spec_verify_desc* d, int32_t num_exits, Plan* p) {
   }
   p->ns = (p->nt + p->tps - 1) / p->tps;
   if (B * p->ns > INT32_MAX) return fail(SV_ERR_UNSUPPORTED, "batch too large for one call");
-  // two slice counters, the lazy final exit's stage-1 counts, and its list of
-  // L_f rows to stream (a count, then up to B * (k + 1) row ids)
-  p->seq_bytes =
-      B > 0 ? ((static_cast<size_t>(B) * (3 + k + 1) + 1) * sizeof(int32_t) + 255) / 256 * 256 : 0;
+  // two slice counters and the lazy call's stage-1 counts per sequence, then
+  // its row list: a count and up to B * (3k + 2) row ids (per sequence at most
+  // the L_d / L_i rows past the stage-1 window and every L_f row, or L_f rows
+  // 0..a1)
+  p->seq_bytes = B > 0 ? ((static_cast<size_t>(B) * (3 * k + 5) + 1) * sizeof(int32_t) + 255) /
+                             256 * 256
+                       : 0;
   p->tile_bytes = (static_cast<size_t>(B) * 2 * p->nt * sizeof(float) + 255) / 256 * 256;
   const size_t n_part = static_cast<size_t>(p->rows_total) * p->nc;
   p->part_bytes = (n_part * sizeof(sv::Partial) + 255) / 256 * 256;
@@ -282,39 +285,46 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.flags = flags;
   sa.tpart = want_entropy ? tpart : nullptr;
   int32_t* lazy_a1 = lazy ? seqw + 2 * B : nullptr;
-  int32_t* lf_count = seqw + 3 * B;       // lazy: L_f rows listed by stage 1
-  int32_t* lf_list = seqw + 3 * B + 1;
-  if (diag && diag->stats_begin) {
-    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
-    if (err != hipSuccess) return device_error(err, "event record");
-  }
+  const int k = desc->num_draft;
+  int32_t* list_count = seqw + 3 * B;   // lazy: rows listed by the window pass
+  int32_t* row_list = seqw + 3 * B + 1;
+  // lazy: the stage-1 window, rows j < r0 of L_d and j < r1 of L_i (with the
+  // bonus row when the window covers every draft)
+  const int r0 = std::min(std::max(window, 1), k), r1 = r0 + (r0 == k ? 1 : 0);
+  hipEvent_t ev_begin = diag ? static_cast<hipEvent_t>(diag->stats_begin) : nullptr;
+  hipEvent_t ev_end = diag ? static_cast<hipEvent_t>(diag->stats_end) : nullptr;
   if (!lazy) {
-    err = sv::launch_stats(sa, p.rows_total, st);
+    err = sv::launch_stats(sa, p.rows_total, st, ev_begin, ev_end);
     if (err != hipSuccess) return device_error(err, "row statistics launch");
   } else {
-    // L_d and L_i rows, stage 1 alone, then the L_f rows stage 2 can reach
-    err = sv::launch_stats(sa, p.exit_row0[2], st);
+    // the L_d and L_i rows of the first N_i positions; stage 1 on them lists
+    // the rows still needed (L_f rows 0..a1, or, for a sequence that accepted
+    // all N_i drafts, the rest of its L_d / L_i rows and all of its L_f rows),
+    // which the list-mode statistics then stream
+    sv::StatsArgs sw = sa;
+    sw.win_b = B;
+    sw.win_r0 = r0;
+    sw.win_r1 = r1;
+    err = sv::launch_stats(sw, static_cast<int64_t>(B) * (r0 + r1), st, ev_begin, nullptr);
     if (err != hipSuccess) return device_error(err, "row statistics launch");
   }
   sv::VerifyArgs va{};
   if (lazy) {
     va = stage1_args(desc, p, logits, partials, tokens, temperature, flags);
     va.stage1_only = 1;
+    va.stage1_window = r0;
     va.lazy_a1 = lazy_a1;
-    va.row_list_out = lf_list;
-    va.row_count_out = lf_count;
+    va.row_list_out = row_list;
+    va.row_count_out = list_count;
     err = sv::launch_verify(va, st);
     if (err != hipSuccess) return device_error(err, "stage-1 launch");
-    sv::StatsArgs sf = sa;   // the listed L_f rows only
-    sf.n_clear = 0;
-    sf.row_list = lf_list;
-    sf.row_count = lf_count;
-    err = sv::launch_stats_list(sf, (p.rows_total - p.exit_row0[2]) * p.nc, st);
-    if (err != hipSuccess) return device_error(err, "final-exit statistics launch");
-  }
-  if (diag && diag->stats_end) {
-    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
-    if (err != hipSuccess) return device_error(err, "event record");
+    sv::StatsArgs sl = sa;   // the listed rows only
+    sl.n_clear = 0;
+    sl.row_list = row_list;
+    sl.row_count = list_count;
+    const int64_t per_seq = std::max(3 * k, k + 1);
+    err = sv::launch_stats_list(sl, static_cast<int64_t>(B) * per_seq * p.nc, st, nullptr, ev_end);
+    if (err != hipSuccess) return device_error(err, "listed row statistics launch");
   }
 
   va = sv::VerifyArgs{};
@@ -532,16 +542,9 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
   g.temperature = temperature;
   g.partials = part;
   g.gath = gath;
-  if (diag && diag->stats_begin) {
-    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_begin), st);
-    if (err != hipSuccess) return device_error(err, "event record");
-  }
-  err = sv::launch_lmhead_stats(g, st);
+  err = sv::launch_lmhead_stats(g, st, diag ? static_cast<hipEvent_t>(diag->stats_begin) : nullptr,
+                                diag ? static_cast<hipEvent_t>(diag->stats_end) : nullptr);
   if (err != hipSuccess) return device_error(err, "LM-head statistics launch");
-  if (diag && diag->stats_end) {
-    err = hipEventRecord(static_cast<hipEvent_t>(diag->stats_end), st);
-    if (err != hipSuccess) return device_error(err, "event record");
-  }
 
   sv::MergeArgs ma{part, merged, g.M, p.n_tiles, seqw, 2 * B, flags};
   err = sv::launch_merge(ma, st);

@@ -441,9 +441,10 @@ unsigned gemm_grid(const GemmArgs& a) {
 
 }  // namespace
 
-hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((lmhead_gemm<StatsCfg, false>), dim3(gemm_grid<StatsCfg>(a)),
-                     dim3(StatsCfg::GT), 0, st, a);
+hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st, hipEvent_t ev_start,
+                               hipEvent_t ev_stop) {
+  launch_timed(lmhead_gemm<StatsCfg, false>, dim3(gemm_grid<StatsCfg>(a)), dim3(StatsCfg::GT), st,
+               ev_start, ev_stop, a);
   return hipGetLastError();
 }
 

@@ -26,7 +26,17 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   }
   const int rel = blockIdx.x / a.nc;
   const int chunk = blockIdx.x - rel * a.nc;
-  const int row = a.row_begin + rel;
+  int row = a.row_begin + rel;
+  if (a.win_b > 0) {   // rows j < win_r0 of exit 0, then rows j < win_r1 of exit 1
+    const int rows0 = a.win_b * a.win_r0;
+    if (rel < rows0) {
+      const int b0 = rel / a.win_r0;
+      row = a.exit_row0[0] + b0 * a.exit_pos[0] + (rel - b0 * a.win_r0);
+    } else {
+      const int r = rel - rows0, b1 = r / a.win_r1;
+      row = a.exit_row0[1] + b1 * a.exit_pos[1] + (r - b1 * a.win_r1);
+    }
+  }
   int e = 0;
   if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
   if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
@@ -58,11 +68,13 @@ __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
     if (i < a.n_clear) a.clear_words[i] = 0;
     if (i == 0) a.flags[0] = 0u;
   }
-  const int n_items = *a.row_count * a.nc;
+  // the count and the row ids are uniform: keep them (and all that follows
+  // from them) in scalar registers
+  const int n_items = __builtin_amdgcn_readfirstlane(*a.row_count) * a.nc;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int rel = it / a.nc;
     const int chunk = it - rel * a.nc;
-    const int row = a.row_list[rel];
+    const int row = __builtin_amdgcn_readfirstlane(a.row_list[rel]);
     int e = 0;
     if (a.num_exits > 1 && row >= a.exit_row0[1]) e = 1;
     if (a.num_exits > 2 && row >= a.exit_row0[2]) e = 2;
@@ -82,30 +94,33 @@ __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
 
 }  // namespace
 
-hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st) {
+hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st,
+                             hipEvent_t ev_start, hipEvent_t ev_stop) {
   // two resident workgroups per CU (the looping kernel holds more registers)
   constexpr int64_t kListWorkgroups = 512;
   const int64_t clear_wg = (a.n_clear + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<unsigned>(std::max<int64_t>(
       1, std::max(clear_wg, std::min(max_items, kListWorkgroups)))));
   if (a.dtype == 1)
-    hipLaunchKernelGGL(rowstats_list_kernel<1>, grid, dim3(kThreads), 0, st, a);
+    launch_timed(rowstats_list_kernel<1>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
   else
-    hipLaunchKernelGGL(rowstats_list_kernel<0>, grid, dim3(kThreads), 0, st, a);
+    launch_timed(rowstats_list_kernel<0>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
   return hipGetLastError();
 }
 
-hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st) {
+hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
   const dim3 grid(static_cast<unsigned>(rows_total * a.nc));
+  const dim3 block(kThreads);
   if (a.tpart) {
     if (a.dtype == 1)
-      hipLaunchKernelGGL((rowstats_kernel<1, true>), grid, dim3(kThreads), 0, st, a);
+      launch_timed(rowstats_kernel<1, true>, grid, block, st, ev_start, ev_stop, a);
     else
-      hipLaunchKernelGGL((rowstats_kernel<0, true>), grid, dim3(kThreads), 0, st, a);
+      launch_timed(rowstats_kernel<0, true>, grid, block, st, ev_start, ev_stop, a);
   } else if (a.dtype == 1) {
-    hipLaunchKernelGGL((rowstats_kernel<1, false>), grid, dim3(kThreads), 0, st, a);
+    launch_timed(rowstats_kernel<1, false>, grid, block, st, ev_start, ev_stop, a);
   } else {
-    hipLaunchKernelGGL((rowstats_kernel<0, false>), grid, dim3(kThreads), 0, st, a);
+    launch_timed(rowstats_kernel<0, false>, grid, block, st, ev_start, ev_stop, a);
   }
   return hipGetLastError();
 }

@@ -61,15 +61,19 @@ struct VerifyArgs {
   int64_t draw_ld;
   int32_t decide_only;
   int32_t* stop_rows;
-  // Lazy final exit: a first pass with `stage1_only` writes each sequence's
-  // stage-1 accept count to lazy_a1; the verification then merges only the
-  // L_f rows 0..a1 (the only ones stage 2 reads).  NULL: every row.
+  // Lazy final exit: a first pass with `stage1_only` runs stage 1 over the
+  // positions below stage1_window (the only L_d / L_i rows streamed so far).
+  // Where it fixes a1 (a rejection there, or a window that covers every
+  // draft) it writes lazy_a1 = a1 and lists the L_f rows 0..a1; otherwise it
+  // writes lazy_a1 = -1 and lists the remaining L_d / L_i rows and every L_f
+  // row.  Row ids are global, appended to row_list_out at an atomically
+  // advanced *row_count_out.  The verification then merges L_f rows 0..a1
+  // where lazy_a1 >= 0, every row otherwise.  NULL lazy_a1: every row.
   int32_t stage1_only;
   int32_t* lazy_a1;
-  // ... and appends each sequence's L_f rows 0..a1 (global row ids) to
-  // row_list_out at an atomically advanced *row_count_out (NULL: no list)
   int32_t* row_list_out;
   int32_t* row_count_out;
+  int32_t stage1_window;
   // Flush of pending tentative tokens: a single-stage chain per sequence over
   // its n = flush_lim[b] + 1 pending tokens (0: the sequence is not flushed),
   // q = exit 0 (the pending L_i rows), p = exit 1 (the final exit), Philox
@@ -143,7 +147,8 @@ constexpr int kGemmWM = 2;     // wavefronts of a GEMM workgroup along rows
 constexpr int kGemmWN = 4;     // and along the vocabulary
 constexpr int kGemmKT = 64;    // hidden elements per pipeline step
 
-hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st);
+hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st, hipEvent_t ev_start = nullptr,
+                               hipEvent_t ev_stop = nullptr);
 hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 

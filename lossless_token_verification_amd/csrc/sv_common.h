@@ -4,6 +4,7 @@
 // argument blocks and helpers are in sv_args.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +51,10 @@ struct StatsArgs {
   int32_t n_clear;
   uint32_t* flags;
   int32_t row_begin;       // first row of this launch (rows are launched in order)
+  // Position window (win_b > 0 sequences): the launch covers rows j < win_r0
+  // of exit 0, then rows j < win_r1 of exit 1, win_b * (win_r0 + win_r1) rows
+  // (the lazy call's first stage-1 window).
+  int32_t win_b, win_r0, win_r1;
   // Row entropies requested: per (row, chunk) T = sum 2^(l*s - c) * (l*s - c)
   // beside the partial (same reference c); NULL: not computed.
   double* tpart;
@@ -59,11 +64,26 @@ struct StatsArgs {
   const int32_t* row_count;
 };
 
-hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st);
+// A kernel launch that, given events, has them take the kernel's own start and
+// end times (hipExtLaunchKernelGGL) instead of recording them around it.
+template <typename K, typename A>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t ev_start,
+                         hipEvent_t ev_stop, const A& args) {
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev_start, ev_stop, 0, args);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args);
+}
+
+// ev_start / ev_stop (either may be NULL): events that take the kernel's own
+// start and end times (an extended launch: no marker packets on the stream).
+hipError_t launch_stats(const StatsArgs& a, int64_t rows_total, hipStream_t st,
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // The rows of a.row_list only: a grid of at most max_wg workgroups loops over
 // (listed row, chunk) items, so a launch costs the rows it reads rather than
 // one dispatched workgroup per possible row.
-hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st);
+hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // ---------------------------------------------------------------------------
 // device helpers

@@ -688,13 +688,15 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
           const int64_t base0 = (static_cast<int64_t>(b) * 2 + 0) * diag_pos + j;
           const int64_t base1 = (static_cast<int64_t>(b) * 2 + 1) * diag_pos + j;
           if (a.diag_probs) {
-            a.diag_probs[base0 * 2] = j < k ? p1 : NAN;
-            a.diag_probs[base0 * 2 + 1] = j < k ? q1 : NAN;
+            // tested positions only: stage 1 stops at a1, stage 2 at a2
+            const bool t1 = j < k && j <= a1, t2 = j < a1 && j <= a2p;
+            a.diag_probs[base0 * 2] = t1 ? p1 : NAN;
+            a.diag_probs[base0 * 2 + 1] = t1 ? q1 : NAN;
             // position a1 of stage 2 belongs to the test of y when it happens
             // (one writer per entry: stores from different XCDs are not ordered)
             if (j != a1 || a2p < a1) {
-              a.diag_probs[base1 * 2] = j < a1 ? p2 : NAN;
-              a.diag_probs[base1 * 2 + 1] = j < a1 ? q2 : NAN;
+              a.diag_probs[base1 * 2] = t2 ? p2 : NAN;
+              a.diag_probs[base1 * 2 + 1] = t2 ? q2 : NAN;
             }
           }
           if (a.diag_uniforms) {
@@ -794,11 +796,6 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
             qj = 0.0;
           }
         }
-        if (diag && a.diag_probs && j < diag_pos) {
-          double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + stage) * diag_pos + j) * 2;
-          d[0] = j < n ? pj : NAN;
-          d[1] = j < n ? qj : NAN;
-        }
         if (diag && a.diag_uniforms && j < diag_pos) {
           float* d = a.diag_uniforms + ((static_cast<int64_t>(b) * 2 + stage) * diag_pos + j) * 2;
           d[0] = u;
@@ -815,6 +812,11 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
             acc = __ffsll(rm & wm) - 1;
             break;
           }
+        }
+        if (diag && a.diag_probs && j < diag_pos) {   // tested positions: 0..acc
+          double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + stage) * diag_pos + j) * 2;
+          d[0] = j < n && j <= acc ? pj : NAN;
+          d[1] = j < n && j <= acc ? qj : NAN;
         }
         if (lane == 0) sm.sh[0] = acc;
       }
@@ -998,24 +1000,35 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
       v1 = sm.vs[a2];
     } else {
     if (a.stage1_only) {
-      // lazy final exit, first pass: stage 1 alone, from L_d and L_i
+      // lazy call, stage 1 alone from the L_d and L_i rows of the first
+      // positions: where a draft is rejected there (or the window covers every
+      // draft) a1 is fixed and the L_f rows 0..a1 are listed; otherwise the
+      // remaining L_d / L_i rows and every L_f row of the sequence are listed,
+      // and the final pass decides stage 1 over all positions
       if (!first) return;
+      const int n0 = min(a.stage1_window, k);
       cx.pregather(2);
-      cx.merge_all(k, k + 1, 0);
-      const int s1 = cx.decide(0, 1, k, 0, true, k > 0 ? k : 1, false);
+      cx.merge_all(n0, n0 + (n0 == k ? 1 : 0), 0);
+      const int s1 = cx.decide(0, 1, n0, 0, false, n0 > 0 ? n0 : 1, false);
       if (tid == 0) {
-        a.lazy_a1[b] = s1;
-        if (a.row_list_out) {   // the L_f rows stage 2 can read
-          const int base = atomicAdd(a.row_count_out, s1 + 1);
-          for (int j = 0; j <= s1; ++j)
-            a.row_list_out[base + j] = static_cast<int32_t>(cx.row_index(2, j));
+        const bool fixed = s1 < n0 || n0 == k;
+        const int n_rest = fixed ? 0 : 2 * (k - n0) + 1;
+        const int n_f = fixed ? s1 + 1 : k + 1;
+        a.lazy_a1[b] = fixed ? s1 : -1;
+        const int base = atomicAdd(a.row_count_out, n_rest + n_f);
+        for (int j = n0; j < n0 + n_rest; ++j) {   // L_d rows n0..k-1, L_i rows n0..k
+          const int e = j < k ? 0 : 1, pos = j < k ? j : j - (k - n0);
+          a.row_list_out[base + j - n0] = static_cast<int32_t>(cx.row_index(e, pos));
         }
+        for (int j = 0; j < n_f; ++j)
+          a.row_list_out[base + n_rest + j] = static_cast<int32_t>(cx.row_index(2, j));
       }
       return;
     }
     cx.pregather(a.hier ? 3 : 2);
     // stage 2 reads L_f rows 0..a1 only (all of them unless the final exit is lazy)
-    cx.merge_all(k, k + 1, a.hier ? (a.lazy_a1 ? a.lazy_a1[b] + 1 : k + 1) : 0);
+    // (lazy: a1 where the window pass fixed it, else every L_f row was listed)
+    cx.merge_all(k, k + 1, a.hier ? (a.lazy_a1 && a.lazy_a1[b] >= 0 ? a.lazy_a1[b] + 1 : k + 1) : 0);
     if (a.hier) {
       const int2 r = cx.decide_pre(a.window, first);
       a1 = r.x;

@@ -80,6 +80,10 @@ def _check_probs(gpu, ref, keep, bf16, report):
     max_p = max_d = 0.0
     for b in keep:
         for s, info in enumerate(_stage_infos(ref["infos"][b])):
+            n_t = len(info["tests"])
+            # positions after a stage's stop were not tested: NaN
+            rest = probs[b, s, n_t:]
+            assert np.isnan(rest).all(), (b, s, rest)
             for j, (u, p, q) in enumerate(info["tests"]):
                 gp, gq = probs[b, s, j]
                 for o, gv in ((p, gp), (q, gq)):

@@ -62,11 +62,11 @@ def test_workspace_size_formula(sv):
         return pad(rows * nc * 16) + pad(rows * nc * 8) + B * 2 * (k + 1) * nc * 72
 
     assert sv.workspace_bytes(256, 8, 128256, 1, 3) == \
-        256 + pad((256 * 12 + 1) * 4) + pad(256 * 2 * tiles(128256, 512) * 4) + parts(256 * 26, 4, 256, 8)
+        256 + pad((256 * 29 + 1) * 4) + pad(256 * 2 * tiles(128256, 512) * 4) + parts(256 * 26, 4, 256, 8)
     assert sv.workspace_bytes(64, 4, 32000, 1, 2) == \
-        256 + pad((64 * 8 + 1) * 4) + pad(64 * 2 * tiles(32000, 512) * 4) + parts(64 * 9, 1, 64, 4)
+        256 + pad((64 * 17 + 1) * 4) + pad(64 * 2 * tiles(32000, 512) * 4) + parts(64 * 9, 1, 64, 4)
     assert sv.workspace_bytes(32, 5, 151936, 0, 2) == \
-        256 + pad((32 * 9 + 1) * 4) + pad(32 * 2 * tiles(151936, 256) * 4) + parts(32 * 11, 10, 32, 5)
+        256 + pad((32 * 20 + 1) * 4) + pad(32 * 2 * tiles(151936, 256) * 4) + parts(32 * 11, 10, 32, 5)
     assert sv.workspace_bytes(0, 4, 10, 0, 2) == 256
     assert sv.workspace_bytes(1, 64, 10, 0, 2) == 0        # invalid descriptor -> 0
 
