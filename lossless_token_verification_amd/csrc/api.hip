@@ -226,7 +226,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
                    int32_t* accept_len, int32_t* accept_len_final, int32_t* out_tokens,
                    int32_t* num_emitted, int32_t* num_drop, int32_t* packed, int32_t* cu_offsets,
                    void* workspace, size_t workspace_bytes, const spec_verify_diag* diag,
-                   void* hip_stream, const KvRollback* kv = nullptr, bool lazy = false) {
+                   void* hip_stream, const KvRollback* kv = nullptr, bool lazy = false,
+                   bool clear_round = false) {
   Plan p;
   SV_TRY(make_plan(desc, num_exits, &p));
   if (num_exits == 3 && window < 1) return fail(SV_ERR_INVALID_ARG, "window < 1");
@@ -281,7 +282,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   sa.temperature = temperature;
   sa.partials = partials;
   sa.clear_words = seqw;   // slice counters (and, lazy, the stage-1 counts and list count)
-  sa.n_clear = lazy ? 3 * B + 1 : 2 * B;
+  // (a tentative round: its append's arrival counters in the third block)
+  sa.n_clear = lazy ? 3 * B + 1 : (clear_round ? 3 * B : 2 * B);
   sa.flags = flags;
   sa.tpart = want_entropy ? tpart : nullptr;
   int32_t* lazy_a1 = lazy ? seqw + 2 * B : nullptr;
@@ -670,7 +672,8 @@ int32_t run_round(const spec_verify_desc* desc, const void* ld, const void* li,
   int32_t* n_out = reinterpret_cast<int32_t*>(ws + off + pad256(static_cast<size_t>(B) * (k + 1) * 4));
   const void* logits[3] = {ld, li, nullptr};
   SV_TRY(run_verify(desc, 2, 1, logits, tokens, temperature, accept_len, nullptr, t_out, n_out,
-                    num_drop, nullptr, nullptr, workspace, t.round.ws_bytes, nullptr, hip_stream));
+                    num_drop, nullptr, nullptr, workspace, t.round.ws_bytes, nullptr, hip_stream,
+                    nullptr, false, true));
   if (B == 0) return SV_OK;
   sv::PendArgs pa{};
   pa.B = B;
@@ -688,6 +691,8 @@ int32_t run_round(const spec_verify_desc* desc, const void* ld, const void* li,
   pa.tokens = pending->tokens;
   pa.rows = pending->rows;
   pa.flags = reinterpret_cast<uint32_t*>(ws);
+  // the third block of per-sequence words (cleared by the statistics launch)
+  pa.arrive = reinterpret_cast<int32_t*>(ws + sv::kFlagsBytes) + 2 * B;
   const hipError_t err = sv::launch_pending_append(pa, static_cast<hipStream_t>(hip_stream));
   if (err != hipSuccess) return device_error(err, "pending append launch");
   return SV_OK;
@@ -801,8 +806,6 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
   va.flush_lim = lim;
   err = sv::launch_verify(va, st);
   if (err != hipSuccess) return device_error(err, "flush verify launch");
-  err = sv::launch_flush_reset(pa, st);
-  if (err != hipSuccess) return device_error(err, "flush reset launch");
   return SV_OK;
 }
 

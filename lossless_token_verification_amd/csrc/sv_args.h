@@ -200,12 +200,13 @@ struct PendArgs {
   int32_t row0_q, row0_p;    // flush: first global row of the pending rows and of L_f
   int32_t* row_list;         // flush: the rows to stream (pending rows, then L_f rows,
   int32_t* row_count;        //   of each flushed sequence in order) and their number
+  int32_t* arrive;           // [B] round: workgroups of the append done so far (zeroed
+                             //   by the round's statistics launch)
   uint32_t* flags;
 };
 constexpr uint32_t kFlagPendingFull = 4u;
 hipError_t launch_pending_append(const PendArgs& a, hipStream_t st);
 hipError_t launch_flush_prep(const PendArgs& a, hipStream_t st);
-hipError_t launch_flush_reset(const PendArgs& a, hipStream_t st);
 
 hipError_t launch_entropy(const ByArgs& a, hipStream_t st);
 hipError_t launch_outcome(const ByArgs& a, hipStream_t st);

@@ -15,70 +15,76 @@ namespace sv {
 
 namespace {
 
-// One workgroup per (sequence, position j <= a1, 64 KiB chunk): copies that
-// chunk of L_i row j to pending row count + j.  Rows that would not fit are
-// skipped (the count update flags them).
+// One workgroup per (sequence, position j <= k, 64 KiB chunk): copies that
+// chunk of L_i row j to pending row count + j (rows that would not fit are
+// skipped; the count update flags them); workgroups past a1 exit at once.
+// The (a1 + 1) x chunks others read the old count before they arrive on the
+// sequence's counter; the last to arrive appends the a1 + 1 output tokens
+// and advances the count.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void append_rows_kernel(PendArgs a) {
   constexpr int ES = DT == 1 ? 2 : 4;
   constexpr int VPE = 16 / ES;
   constexpr int CE = kChunkBytes / ES;
+  __shared__ int c0_sh;
   const int ch = blockIdx.x % a.nch;
   const int rest = blockIdx.x / a.nch;
   const int j = rest % (a.k + 1), b = rest / (a.k + 1);
   if (a.active && !a.active[b]) return;
-  if (j > a.a1[b]) return;
-  const int dst = min(max(a.count[b], 0), a.cap) + j;
-  if (dst >= a.cap) return;
-  const char* src = static_cast<const char*>(a.li) + (static_cast<int64_t>(b) * (a.k + 1) + j) * a.ld * ES;
-  char* out = static_cast<char*>(a.rows) + (static_cast<int64_t>(b) * a.cap + dst) * a.ld * ES;
-  const int e0 = ch * CE, e1 = min(a.V, e0 + CE);
+  const int a1 = a.a1[b];
+  if (j > a1) return;
   const int tid = threadIdx.x;
-  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(out)) & 15) == 0) {
-    const int nfull = (e1 - e0) / VPE;
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(src) + e0 / VPE;
-    u32x4* d4 = reinterpret_cast<u32x4*>(out) + e0 / VPE;
-    for (int v = tid; v < nfull; v += kThreads) d4[v] = __builtin_nontemporal_load(s4 + v);
-    for (int e = e0 + nfull * VPE + tid; e < e1; e += kThreads) {
-      if constexpr (DT == 1)
-        reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
-      else
-        reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
-    }
-  } else {
-    for (int e = e0 + tid; e < e1; e += kThreads) {
-      if constexpr (DT == 1)
-        reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
-      else
-        reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
+  if (tid == 0) c0_sh = min(max(a.count[b], 0), a.cap);
+  __syncthreads();
+  const int c0 = c0_sh;   // the old count, read before this workgroup arrives
+  const int dst = c0 + j;
+  if (dst < a.cap) {
+    const char* src =
+        static_cast<const char*>(a.li) + (static_cast<int64_t>(b) * (a.k + 1) + j) * a.ld * ES;
+    char* out = static_cast<char*>(a.rows) + (static_cast<int64_t>(b) * a.cap + dst) * a.ld * ES;
+    const int e0 = ch * CE, e1 = min(a.V, e0 + CE);
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(out)) & 15) == 0) {
+      const int nfull = (e1 - e0) / VPE;
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(src) + e0 / VPE;
+      u32x4* d4 = reinterpret_cast<u32x4*>(out) + e0 / VPE;
+      for (int v = tid; v < nfull; v += kThreads) d4[v] = __builtin_nontemporal_load(s4 + v);
+      for (int e = e0 + nfull * VPE + tid; e < e1; e += kThreads) {
+        if constexpr (DT == 1)
+          reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+        else
+          reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
+      }
+    } else {
+      for (int e = e0 + tid; e < e1; e += kThreads) {
+        if constexpr (DT == 1)
+          reinterpret_cast<uint16_t*>(out)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+        else
+          reinterpret_cast<uint32_t*>(out)[e] = reinterpret_cast<const uint32_t*>(src)[e];
+      }
     }
   }
-}
-
-// One thread per sequence: appends the a1 + 1 output tokens and advances the
-// count (after the row copies, which read the old count).
-__global__ __launch_bounds__(kThreads) void append_tokens_kernel(PendArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.B) return;
-  if (a.active && !a.active[b]) return;
-  const int c = min(max(a.count[b], 0), a.cap);
-  int n = a.a1[b] + 1;
-  const int room = a.cap - c;
+  if (tid != 0) return;
+  const int total = (a1 + 1) * a.nch;
+  if (atomicAdd(a.arrive + b, 1) != total - 1) return;
+  // every copying workgroup of the sequence has read the old count
+  int n = a1 + 1;
+  const int room = a.cap - c0;
   if (n > room) {
     atomicOr(a.flags, kFlagPendingFull);
     n = room > 0 ? room : 0;
   }
   for (int i = 0; i < n; ++i)
-    a.tokens[static_cast<int64_t>(b) * a.cap + c + i] = a.t_out[static_cast<int64_t>(b) * (a.k + 1) + i];
-  a.count[b] = c + n;
+    a.tokens[static_cast<int64_t>(b) * a.cap + c0 + i] = a.t_out[static_cast<int64_t>(b) * (a.k + 1) + i];
+  a.count[b] = c0 + n;
 }
 
-// Flush bookkeeping.  prep (one workgroup): lim = last pending position of a
+// Flush bookkeeping (one workgroup): lim = last pending position of a
 // sequence with at least max(1, min_pending) pending tokens, else -1, and the
 // list of rows the flush streams -- each flushed sequence's pending rows 0..c-1
 // then its L_f rows 0..c-1, sequences in order (a workgroup-wide exclusive scan
-// of 2c per batch of 256 sequences).  reset: the flushed sequences' pending
-// state empties.
+// of 2c per batch of 256 sequences).  The flushed sequences' counts drop to 0
+// here: the rest of the flush reads the limits, the list and the pending
+// tokens and rows, never the count.
 __global__ __launch_bounds__(kThreads) void flush_prep_kernel(PendArgs a) {
   __shared__ int scan[kThreads];
   const int tid = threadIdx.x;
@@ -90,6 +96,7 @@ __global__ __launch_bounds__(kThreads) void flush_prep_kernel(PendArgs a) {
       const int c = min(max(a.count[b], 0), a.cap);
       n = c >= max(1, a.min_pending) ? c : 0;
       a.lim[b] = n - 1;
+      if (n > 0) a.count[b] = 0;
     }
     scan[tid] = 2 * n;
     __syncthreads();
@@ -110,37 +117,21 @@ __global__ __launch_bounds__(kThreads) void flush_prep_kernel(PendArgs a) {
   if (tid == 0) *a.row_count = base;
 }
 
-__global__ __launch_bounds__(kThreads) void flush_reset_kernel(PendArgs a) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= a.B) return;
-  if (a.lim[b] >= 0) a.count[b] = 0;
-}
-
-unsigned blocks_for(int n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
 
 }  // namespace
 
 hipError_t launch_pending_append(const PendArgs& a, hipStream_t st) {
   const int64_t wg = static_cast<int64_t>(a.B) * (a.k + 1) * a.nch;
-  if (wg > 0) {
-    if (a.dtype == 1)
-      hipLaunchKernelGGL(append_rows_kernel<1>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(append_rows_kernel<0>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(append_tokens_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
+  if (wg == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(append_rows_kernel<1>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_rows_kernel<0>, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_flush_prep(const PendArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(flush_prep_kernel, dim3(1), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_flush_reset(const PendArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(flush_reset_kernel, dim3(blocks_for(a.B)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
