@@ -212,6 +212,25 @@ def _traffic(launch_bytes):
         return None
 
 
+def _draw_and_sequential_bytes(out, w, B, k, V):
+    """Bytes beside the headline, from one step's outputs (bf16 rows of V):
+    the rows the draws re-read after the stream -- L_i, L_d (none for the
+    bonus) and L_f at a1 when stage 2 reaches y, L_f and L_i at a2 when it
+    rejects a draft before a1, none for a greedy sequence -- and the rows a
+    sequential verification would have to read: L_d and L_i up to a1, L_f up
+    to stage 2's stop."""
+    import numpy as np
+    a1 = out["accept_len_inter"].cpu().numpy().astype(np.int64)
+    a2 = out["accept_len_final"].cpu().numpy().astype(np.int64)
+    t = w["temperature"]
+    sampled = (t.cpu().numpy() > 0) if t is not None else np.ones(B, dtype=bool)
+    early = a2 < a1
+    draw_rows = np.where(early, 2, np.where(a1 < k, 3, 2)) * sampled
+    seq_rows = np.minimum(a1 + 1, k) + (a1 + 1) + (np.minimum(a1, a2) + 1)
+    row_bytes = V * 2
+    return int(draw_rows.sum()) * row_bytes, int(seq_rows.sum()) * row_bytes
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -565,6 +584,7 @@ def main():
     step_gbps = launch_bytes / (ms_step / 1e3) / 1e9
     k1_gbps = launch_bytes / (k1_avg / 1e3) / 1e9
     traffic = _traffic(launch_bytes)
+    reread, seq_bound = _draw_and_sequential_bytes(bufs["out"], w, B, k, V)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -585,6 +605,8 @@ def main():
         "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_of_peak_step": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "draw_reread_bytes_last_step": reread,
+        "sequential_lower_bound_bytes_last_step": seq_bound,
         "roofline": {"bound": "hbm", "kernel": "rowstats_kernel<bf16>",
                      "achieved": round(k1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
