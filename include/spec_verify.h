@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 2
+#define SPEC_VERIFY_ABI_VERSION 3
 
 /* Status codes. */
 #define SV_OK 0
@@ -153,6 +153,13 @@ typedef struct {
  *             ("Speculative Speculative Decoding", gist.science 2603.03251,
  *             section 2 items 1-2, section 3.A and 3.B).  It re-reads the
  *             rows of every tested position once more after the statistics.
+ *
+ * Row statistics (spec_verify_single, spec_verify_hier,
+ * spec_verify_hier_rollback; SV_ERR_UNSUPPORTED from the lazy and LM-head
+ * calls): row_log2z and row_argmax give every row's merged softmax statistics
+ * in the order of the entropy field, so that a caller can form any
+ * probability of any row from the logits; written by the verification launch
+ * at no extra stream cost.
  */
 typedef struct {
   float* uniforms;   /* [B, 2, k+1, 2]: (u, v) of each position                   */
@@ -170,6 +177,12 @@ typedef struct {
   int32_t* residual_tokens;    /* [B, 2, k+1, top_m]: largest residual tokens    */
   float* residual_mass;        /* [B, 2, k+1, top_m]: their r_v                  */
   int32_t top_m;               /* 1..SV_MAX_TOP_M when either residual field is set */
+  double* row_log2z;           /* [rows of every exit]: the merged normalizer of each
+                                  row in the kernel's base-2 units, z = c + log2 S, so
+                                  that P_v = 2^(l_v * s - z) with s = log2(e) / tau
+                                  rounded to float; NaN for greedy rows             */
+  int32_t* row_argmax;         /* [rows of every exit]: greedy rows' argmax (lowest
+                                  index on ties); -1 for sampled rows               */
 } spec_verify_diag;
 
 /* Version of this header's ABI (SPEC_VERIFY_ABI_VERSION). */

@@ -67,7 +67,8 @@ class Diag(ctypes.Structure):
                 ("draws", ctypes.c_void_p), ("stats_begin", ctypes.c_void_p),
                 ("stats_end", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
                 ("accept_mass", ctypes.c_void_p), ("residual_tokens", ctypes.c_void_p),
-                ("residual_mass", ctypes.c_void_p), ("top_m", ctypes.c_int32)]
+                ("residual_mass", ctypes.c_void_p), ("top_m", ctypes.c_int32),
+                ("row_log2z", ctypes.c_void_p), ("row_argmax", ctypes.c_void_p)]
 
 
 class Pending(ctypes.Structure):
@@ -224,13 +225,16 @@ def _diag_buffers(B, k, device):
                 draws=torch.empty((B, 2, 4), dtype=torch.float64, device=device))
 
 
-def _make_diag(diag, events, B, k, dev, out, rows=0, entropy=False, outcome=False, top_m=0):
+def _make_diag(diag, events, B, k, dev, out, rows=0, entropy=False, outcome=False, top_m=0,
+               row_stats=False):
     """Diag struct: export buffers when ``diag``; ``events`` = (begin, end)
-    hipEvent_t handles (ints) recorded around the row-statistics kernel;
-    by-product outputs when ``entropy`` (out["entropy"], one float per row of
-    every exit) or ``outcome`` (out["accept_mass"] [B, 2, k+1] and, for
-    top_m > 0, out["residual_tokens"] / out["residual_mass"] [B, 2, k+1, top_m])."""
-    if not diag and events is None and not entropy and not outcome:
+    hipEvent_t handles (ints) that take the row-statistics kernel's start and
+    end times; by-product outputs when ``entropy`` (out["entropy"], one float
+    per row of every exit) or ``outcome`` (out["accept_mass"] [B, 2, k+1] and,
+    for top_m > 0, out["residual_tokens"] / out["residual_mass"]
+    [B, 2, k+1, top_m]); every row's merged statistics when ``row_stats``
+    (out["row_log2z"] float64 and out["row_argmax"] int32, one per row)."""
+    if not diag and events is None and not entropy and not outcome and not row_stats:
         return None
     dg = Diag()
     if diag:
@@ -254,6 +258,11 @@ def _make_diag(diag, events, B, k, dev, out, rows=0, entropy=False, outcome=Fals
             dg.residual_tokens = out["residual_tokens"].data_ptr()
             dg.residual_mass = out["residual_mass"].data_ptr()
             dg.top_m = int(top_m)
+    if row_stats:
+        out["row_log2z"] = torch.empty((max(1, rows),), dtype=torch.float64, device=dev)
+        out["row_argmax"] = torch.empty((max(1, rows),), dtype=torch.int32, device=dev)
+        dg.row_log2z = out["row_log2z"].data_ptr()
+        dg.row_argmax = out["row_argmax"].data_ptr()
     return dg
 
 
@@ -269,7 +278,7 @@ def _prep_common(draft_tokens, temperature, B, k, device):
 
 def spec_verify_single(draft_logits, target_logits, draft_tokens, temperature=None, *, seed=0,
                        offset=0, packed=False, diag=False, workspace=None, events=None,
-                       entropy=False, outcome=False, top_m=0):
+                       entropy=False, outcome=False, top_m=0, row_stats=False):
     """Single-stage verify (standard rule).  Returns a dict of device tensors:
     accept_len, out_tokens [B, k+1] (-1 padded), num_emitted, num_drop, and
     packed_tokens / cu_offsets, diag buffers and by-products (``entropy``,
@@ -291,7 +300,8 @@ def spec_verify_single(draft_logits, target_logits, draft_tokens, temperature=No
     if packed:
         out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
         out["cu_offsets"] = _int_out((B + 1,), dev)
-    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m,
+                    row_stats)
     _check(lib.spec_verify_single(
         ctypes.byref(desc), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
@@ -314,7 +324,8 @@ def _bf16_rows(t, name, shape, device):
 
 def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperature=None, *,
                               seed=0, offset=0, packed=False, diag=False, workspace=None,
-                              events=None, out=None, entropy=False, outcome=False, top_m=0):
+                              events=None, out=None, entropy=False, outcome=False, top_m=0,
+                              row_stats=False):
     """Single-stage verify through a linear LM head W [V, d] (one d-vector per
     vocabulary entry): q from h_draft [B, k, d], p from h_target [B, k+1, d].
     Returns the same dict as spec_verify_single.  ``out`` reuses the output
@@ -342,7 +353,8 @@ def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperat
             out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
             out["cu_offsets"] = _int_out((B + 1,), dev)
     out["workspace"] = ws
-    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (2 * k + 1), entropy, outcome, top_m,
+                    row_stats)
     _check(lib.spec_verify_lmhead_single(
         ctypes.byref(desc), d, _ptr(h_draft), _ptr(h_target), _ptr(w_vocab),
         _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
@@ -354,7 +366,7 @@ def spec_verify_lmhead_single(h_draft, h_target, w_vocab, draft_tokens, temperat
 
 def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=None, *,
                      window=4, seed=0, offset=0, packed=False, diag=False, workspace=None,
-                     events=None, entropy=False, outcome=False, top_m=0):
+                     events=None, entropy=False, outcome=False, top_m=0, row_stats=False):
     """HiSpec two-stage verify L_d -> L_i -> L_f.  Returns a dict of device
     tensors: accept_len_inter (a1), accept_len_final (a2), out_tokens,
     num_emitted, num_drop (+ packed / diag on request).  Asynchronous."""
@@ -377,7 +389,8 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
     if packed:
         out["packed_tokens"] = _int_out((max(1, B * (k + 1)),), dev)
         out["cu_offsets"] = _int_out((B + 1,), dev)
-    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m,
+                    row_stats)
     _check(lib.spec_verify_hier(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
         _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len_inter"]),
@@ -390,7 +403,8 @@ def spec_verify_hier(ld_logits, li_logits, lf_logits, draft_tokens, temperature=
 def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
                               block_table, seq_lens, *, block_size, max_freed, window=4,
                               seed=0, offset=0, diag=False, workspace=None, events=None,
-                              out=None, entropy=False, outcome=False, top_m=0, _lazy=False):
+                              out=None, entropy=False, outcome=False, top_m=0, row_stats=False,
+                              _lazy=False):
     """spec_verify_hier plus the paged-KV rollback of block_table / seq_lens
     (in place) in the same launches.  Returns the spec_verify_hier dict plus
     freed_blocks [B, max_freed] and num_freed [B].  ``out``: a dict returned
@@ -425,7 +439,8 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
         if tuple(out["out_tokens"].shape) != (B, k + 1) or \
                 tuple(out["freed_blocks"].shape) != (B, max_freed):
             raise ValueError("out buffers do not match this call's shapes")
-    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m)
+    dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m,
+                    row_stats)
     fn = lib.spec_verify_hier_rollback_lazy if _lazy else lib.spec_verify_hier_rollback
     _check(fn(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),

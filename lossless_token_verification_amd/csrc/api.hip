@@ -133,6 +133,7 @@ bool wants_outcome(const spec_verify_diag* d) {
   return d && (d->accept_mass || d->residual_tokens || d->residual_mass);
 }
 bool wants_byproducts(const spec_verify_diag* d) { return d && (d->entropy || wants_outcome(d)); }
+bool wants_row_stats(const spec_verify_diag* d) { return d && (d->row_log2z || d->row_argmax); }
 
 int32_t check_diag(const spec_verify_diag* diag) {
   if (!diag) return SV_OK;
@@ -150,6 +151,10 @@ int32_t check_diag(const spec_verify_diag* diag) {
     return fail(SV_ERR_MISALIGNED, "diag.residual_tokens not 4-byte aligned");
   if (diag->residual_mass && !aligned_to(diag->residual_mass, 4))
     return fail(SV_ERR_MISALIGNED, "diag.residual_mass not 4-byte aligned");
+  if (diag->row_log2z && !aligned_to(diag->row_log2z, 8))
+    return fail(SV_ERR_MISALIGNED, "diag.row_log2z not 8-byte aligned");
+  if (diag->row_argmax && !aligned_to(diag->row_argmax, 4))
+    return fail(SV_ERR_MISALIGNED, "diag.row_argmax not 4-byte aligned");
   if ((diag->residual_tokens || diag->residual_mass) &&
       (diag->top_m < 1 || diag->top_m > SV_MAX_TOP_M))
     return fail(SV_ERR_INVALID_ARG, "diag.top_m must be in [1, " + std::to_string(SV_MAX_TOP_M) + "]");
@@ -247,8 +252,9 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
   if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
   SV_TRY(check_diag(diag));
-  if (lazy && wants_byproducts(diag))
-    return fail(SV_ERR_UNSUPPORTED, "the lazy final exit does not stream every row: no by-products");
+  if (lazy && (wants_byproducts(diag) || wants_row_stats(diag)))
+    return fail(SV_ERR_UNSUPPORTED,
+                "the lazy final exit does not stream every row: no by-products or row statistics");
   SV_TRY(check_workspace(p, workspace, workspace_bytes));
   if (kv)
     SV_TRY(check_kv(desc->batch, kv->max_blocks, kv->block_size, kv->table, kv->lens, nullptr,
@@ -364,6 +370,8 @@ int32_t run_verify(const spec_verify_desc* desc, int32_t num_exits, int32_t wind
   va.diag_uniforms = diag ? diag->uniforms : nullptr;
   va.diag_probs = diag ? diag->probs : nullptr;
   va.diag_draws = diag ? diag->draws : nullptr;
+  va.row_log2z = diag ? diag->row_log2z : nullptr;
+  va.row_argmax = diag ? diag->row_argmax : nullptr;
   va.flags = flags;
   if (kv) {
     va.kv_table = kv->table;
@@ -501,8 +509,9 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
   SV_TRY(check_i32(cu_offsets, packed != nullptr, "cu_offsets"));
   if (cu_offsets && !packed) return fail(SV_ERR_INVALID_ARG, "cu_offsets without packed_tokens");
   SV_TRY(check_diag(diag));
-  if (wants_byproducts(diag))
-    return fail(SV_ERR_UNSUPPORTED, "the LM-head path stores no logit rows: no by-products");
+  if (wants_byproducts(diag) || wants_row_stats(diag))
+    return fail(SV_ERR_UNSUPPORTED,
+                "the LM-head path stores no logit rows: no by-products or row statistics");
   if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned_to(workspace, 256)) return fail(SV_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < p.ws_bytes)

@@ -49,6 +49,8 @@ struct VerifyArgs {
   int32_t* num_drop;
   float* diag_uniforms;
   double* diag_probs;
+  double* row_log2z;         // [rows]: merged z = c + log2 S per row (NaN: greedy); NULL: none
+  int32_t* row_argmax;       // [rows]: greedy argmax (-1: sampled); NULL: none
   double* diag_draws;
   uint32_t* flags;
   // LM-head path: logits at the drafted tokens come from `gath` (one per row,

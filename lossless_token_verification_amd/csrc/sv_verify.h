@@ -531,10 +531,11 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
     VerifyShared& sm;
     int b, k, V;
     bool greedy;
+    bool rep;   // this workgroup reports the sequence's diagnostics
     float s;
 
     __device__ SeqCtx(const VerifyArgs& a_, VerifyShared& sm_, int b_, bool report)
-        : a(a_), sm(sm_), b(b_) {
+        : a(a_), sm(sm_), b(b_), rep(report) {
       k = a.k;
       V = a.V;
       const float tau = a.temperature ? a.temperature[b] : 1.0f;
@@ -574,6 +575,14 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
              (static_cast<int64_t>(b) * positions(e) + j) * a.ld * RowT<DT>::ES;
     }
 
+    // Export of a merged row's statistics (the reporting workgroup only).
+    __device__ void export_row(int64_t row, const RowStat& r) const {
+      if (!rep) return;
+      if (a.row_log2z)
+        a.row_log2z[row] = greedy || !(r.S > 0.0) ? NAN : static_cast<double>(r.key) + log2(r.S);
+      if (a.row_argmax) a.row_argmax[row] = greedy ? r.amax : -1;
+    }
+
     // Merged statistics of positions [0, n) of exit e into sm.st[e]; threads
     // [t0, t0 + n) do the work.
     __device__ void merge(int e, int n, int t0) {
@@ -581,6 +590,7 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
       if (t >= 0 && t < n) {
         const int64_t row = a.exit_row0[e] + static_cast<int64_t>(b) * positions(e) + t;
         sm.st[e][t] = merge_row(a.partials + row * a.nc, a.nc, greedy);
+        export_row(row, sm.st[e][t]);
       }
     }
 
@@ -612,6 +622,7 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
         const int e = tid < n0 ? 0 : (tid < n0 + n1 ? 1 : 2);
         const int j = tid - (e == 0 ? 0 : (e == 1 ? n0 : n0 + n1));
         sm.st[e][j] = merge_row(stage + tid * nc, nc, greedy);
+        export_row(row_index(e, j), sm.st[e][j]);
       }
       __syncthreads();
     }

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(sv):
 
 def test_version_and_status_strings(sv):
     lib = sv.library()
-    assert sv.abi_version() == 2
+    assert sv.abi_version() == 3
     for code, name in ((0, b"SV_OK"), (1, b"SV_ERR_INVALID_ARG"), (2, b"SV_ERR_UNSUPPORTED"),
                        (3, b"SV_ERR_MISALIGNED"), (4, b"SV_ERR_WORKSPACE"), (5, b"SV_ERR_DEVICE"),
                        (99, b"SV_ERR_UNKNOWN")):
@@ -196,6 +196,18 @@ def test_byproduct_host_checks_without_gpu(sv):
     dg.accept_mass = 0x2000
     db = sv.make_desc(2, 3, 100, 1)
     lm = [ctypes.c_void_p(0x1000)] * 11 + [ctypes.c_void_p(0x10000), 1 << 30]
+    assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *lm, ctypes.byref(dg), None) == \
+        sv.SV_ERR_UNSUPPORTED
+    # row statistics: 8-byte aligned, and only where every row is streamed
+    dg = sv.Diag()
+    dg.row_log2z = 0x2004
+    assert lib.spec_verify_single(ctypes.byref(d), *single, ctypes.byref(dg), None) == \
+        sv.SV_ERR_MISALIGNED
+    assert b"row_log2z" in lib.spec_verify_last_error()
+    dg = sv.Diag()
+    dg.row_argmax = 0x2000
+    assert lib.spec_verify_hier_rollback_lazy(ctypes.byref(d), 4, *hier, ctypes.byref(dg),
+                                              None) == sv.SV_ERR_UNSUPPORTED
     assert lib.spec_verify_lmhead_single(ctypes.byref(db), 64, *lm, ctypes.byref(dg), None) == \
         sv.SV_ERR_UNSUPPORTED
 
