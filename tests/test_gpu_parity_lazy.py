@@ -47,6 +47,8 @@ CASES = [
     (4, 3, 9000, "f32", (0.9,), 2),
     (3, 0, 5000, "bf16", (1.0,), 4),           # k = 0
     (5, 8, 4096, "bf16", (1.0,), 4),
+    (6, 4, 7000, "f32", (1.0,), 4),            # window == k: stage 1 decided in one pass
+    (5, 2, 6000, "bf16", (1.0, 0.0), 7),       # window > k
 ]
 
 
@@ -63,6 +65,30 @@ def test_lazy_equals_dense_and_oracle(sv, case):
         ref = P.oracle_hier(w, trial + 2, trial, window)
         P.compare(lazy, ref, KEYS[:5], range(B), dt == "bf16", report)
     print(f"lazy {case}: {report}")
+
+
+@pytest.mark.parametrize("dt,window", [("bf16", 4), ("f32", 3)])
+def test_lazy_open_sequences(sv, dt, window):
+    """Sequences that accept every draft of the stage-1 window: L_i rows equal
+    to the L_d rows make p / q exactly 1 there.  Half the sequences match over
+    the window only (the rest of their L_d / L_i rows and every L_f row are
+    listed, then stage 1 continues past the window), a quarter over every
+    position (all k drafts accepted, the bonus drawn); the others are left
+    random."""
+    B, k, V = 8, 8, 20011
+    for trial in range(2):
+        w = workloads.make_hier(B, k, V, dtype=dt, temps=(1.0,), window=window,
+                                seed=(84, trial, window), ctx=(16, 64))
+        for b in range(0, B, 2):
+            n = k if b % 4 == 0 else window
+            w["li_logits"][b, :n] = w["ld_logits"][b, :n]
+        dense, lazy = _both(sv, w, 7, trial, window)
+        for key in KEYS + ("table", "lens"):
+            assert torch.equal(dense[key], lazy[key]), key
+        a1 = lazy["accept_len_inter"].cpu().numpy()
+        assert (a1[0::4] == k).all() and (a1[2::4] >= window).all(), a1
+        ref = P.oracle_hier(w, 7, trial, window)
+        P.compare(lazy, ref, KEYS[:5], range(B), dt == "bf16")
 
 
 def test_lazy_and_dense_alternate_on_one_workspace(sv):
