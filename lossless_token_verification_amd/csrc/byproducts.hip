@@ -84,10 +84,13 @@ __global__ __launch_bounds__(kThreads) void entropy_kernel(ByArgs a) {
 //
 // TopList keeps kTopM entries: exact, but its insertion is a chain of
 // compare-swaps that a wavefront runs whenever any lane inserts.  Top2 keeps
-// two entries branch-free, plus `drop`, the largest value it ever discarded:
-// the workgroup's top m taken from the Top2 lists is the chunk's exact top m
-// whenever every discarded value lies strictly below the m-th selected one
-// (otherwise the chunk is scanned again with TopList).
+// two entries branch-free, plus `drop`, the largest value it ever left out;
+// it takes elements four at a time and lists only each group's largest.  The
+// workgroup's top m taken from the Top2 lists is the chunk's exact top m
+// whenever every value left out lies strictly below the m-th selected one
+// (otherwise the chunk is scanned again with TopList): a rare event, since it
+// needs two of the chunk's m largest residuals in one group of four, or three
+// in one thread.
 struct TopList {
   float val[kTopM];
   int32_t idx[kTopM];
@@ -113,6 +116,11 @@ struct TopList {
         idx[i - 1] = ti;
       }
     }
+  }
+  // four consecutive elements (increasing v), each pushed exactly
+  __device__ __forceinline__ void push4(const float (&r)[4], int v0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) push(r[q], v0 + q);
   }
   __device__ __forceinline__ float head_val() const { return val[0]; }
   __device__ __forceinline__ int head_idx() const { return idx[0]; }
@@ -153,6 +161,20 @@ struct Top2 {
     v2 = max(v2, min(r, v1));
     i1 = g1 ? v : i1;
     v1 = max(v1, r);
+  }
+  // Four consecutive elements (increasing v): only the group's largest (the
+  // lowest index among equals) enters the list; the second largest of the
+  // group, the largest of the three left out, joins `drop`.
+  __device__ __forceinline__ void push4(const float (&rf)[4], int v0) {
+    const uint32_t a = __float_as_uint(rf[0]), b = __float_as_uint(rf[1]);
+    const uint32_t c = __float_as_uint(rf[2]), d = __float_as_uint(rf[3]);
+    const bool gb = b > a, gd = d > c;
+    const uint32_t m_ab = max(a, b), m_cd = max(c, d);
+    const int i_ab = gb ? 1 : 0, i_cd = gd ? 3 : 2;
+    const bool g2 = m_cd > m_ab;
+    const uint32_t second = max(max(min(a, b), min(c, d)), min(m_ab, m_cd));
+    drop = max(drop, second);
+    push(__uint_as_float(max(m_ab, m_cd)), v0 + (g2 ? i_cd : i_ab));
   }
   __device__ __forceinline__ float head_val() const { return __uint_as_float(v1); }
   __device__ __forceinline__ int head_idx() const { return i1; }
@@ -261,34 +283,50 @@ __device__ inline double block_sum(double v, PairShared& sh) {
 
 // One pass over elements [e0, e1) of the rows q = base[0], p = base[1],
 // f = base[2] (absent rows alias p): p_v = 2^(l_v s - c) / S per row; stage 0
-// adds min(p, q) to B0 and offers p - min(p, q) to L0, stage 1 likewise for
-// (f, p).  Each thread visits its elements in increasing v.
-template <int DT, class List>
-__device__ inline void pair_scan(const char* const* base, int e0, int e1, bool has0, bool has1,
-                                 float s, const PairShared& sh, List& L0, List& L1, double& B0,
+// (HAS0) adds min(p, q) to B0 and offers p - min(p, q) to L0, stage 1 (HAS1)
+// likewise for (f, p).  Each thread visits its elements in increasing v, four
+// consecutive ones at a time where the rows allow 16-byte loads.
+template <int DT, bool HAS0, bool HAS1, class List>
+__device__ inline void pair_scan(const char* const* base, int e0, int e1, float s,
+                                 const PairShared& sh, List& L0, List& L1, double& B0,
                                  double& B1) {
   constexpr int VPE = DT == 1 ? 8 : 4;
   const int tid = threadIdx.x;
   const float cq = sh.c[0], cp = sh.c[1], cf = sh.c[2];
   const float iq = sh.inv[0], ip = sh.inv[1], i_f = sh.inv[2];
   float b0 = 0.0f, b1 = 0.0f;
-  auto visit = [&](float xq, float xp, float xf, int v) {
+  // residuals of one element for both stages
+  auto elem = [&](float xq, float xp, float xf, float& r0, float& r1) {
     // no contraction: p - min(p, q) must see the same rounded p as the min,
     // so that it is exactly 0 (never negative) where q >= p
 #pragma clang fp contract(off)
     const float pp = __builtin_amdgcn_exp2f(fmaf(xp, s, -cp)) * ip;
-    if (has0) {
+    r0 = r1 = 0.0f;
+    if constexpr (HAS0) {
       const float pq = __builtin_amdgcn_exp2f(fmaf(xq, s, -cq)) * iq;
       const float mn = uminf(pp, pq);
       b0 += mn;
-      L0.push(pp - mn, v);
+      r0 = pp - mn;
     }
-    if (has1) {
+    if constexpr (HAS1) {
       const float pf = __builtin_amdgcn_exp2f(fmaf(xf, s, -cf)) * i_f;
       const float mn = uminf(pp, pf);
       b1 += mn;
-      L1.push(pf - mn, v);
+      r1 = pf - mn;
     }
+  };
+  auto visit = [&](float xq, float xp, float xf, int v) {
+    float r0, r1;
+    elem(xq, xp, xf, r0, r1);
+    if constexpr (HAS0) L0.push(r0, v);
+    if constexpr (HAS1) L1.push(r1, v);
+  };
+  auto visit4 = [&](const float* xq, const float* xp, const float* xf, int v0) {
+    float r0[4], r1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) elem(xq[q], xp[q], xf[q], r0[q], r1[q]);
+    if constexpr (HAS0) L0.push4(r0, v0);
+    if constexpr (HAS1) L1.push4(r1, v0);
   };
   auto flush = [&]() {
     B0 += static_cast<double>(b0);
@@ -298,39 +336,56 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, bool h
   const bool vec = ((reinterpret_cast<uintptr_t>(base[0]) | reinterpret_cast<uintptr_t>(base[1]) |
                      reinterpret_cast<uintptr_t>(base[2])) & 15) == 0;
   if (vec) {
-    // Vectors vi = i * 256 + tid in increasing i; loads issued kBatch vectors
-    // (of each row) ahead of their use, at clamped in-row indices.
-    constexpr int kBatch = 4;
+    // Vectors vi = i * 256 + tid in increasing i, two per row at a time from
+    // two register stages: the loads of the next pair are issued before the
+    // current pair is used (clamped in-row indices past the end).
+    constexpr int kBatch = 2;
     const int nfull = (e1 - e0) / VPE;
     const u32x4* vr[3];
 #pragma unroll
     for (int e = 0; e < 3; ++e) vr[e] = reinterpret_cast<const u32x4*>(base[e]) + e0 / VPE;
-    for (int i0 = 0; i0 < kVecPerThread && i0 * kThreads < nfull; i0 += kBatch) {
-      u32x4 w[3][kBatch];
+    auto fetch = [&](int i0, u32x4 (&w)[3][kBatch]) {
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int vc = min((i0 + q) * kThreads + tid, nfull - 1);
 #pragma unroll
         for (int e = 0; e < 3; ++e) w[e][q] = __builtin_nontemporal_load(vr[e] + vc);
       }
+    };
+    auto use = [&](int i0, const u32x4 (&w)[3][kBatch]) {
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int vi = (i0 + q) * kThreads + tid;
         if (vi >= nfull) continue;
-        const int v0 = e0 + vi * VPE;
-        const uint32_t aq[4] = {w[0][q].x, w[0][q].y, w[0][q].z, w[0][q].w};
-        const uint32_t ap[4] = {w[1][q].x, w[1][q].y, w[1][q].z, w[1][q].w};
-        const uint32_t af[4] = {w[2][q].x, w[2][q].y, w[2][q].z, w[2][q].w};
+        float x[3][VPE];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          if constexpr (DT == 1) {
-            visit(bf16_lo(aq[h]), bf16_lo(ap[h]), bf16_lo(af[h]), v0 + 2 * h);
-            visit(bf16_hi(aq[h]), bf16_hi(ap[h]), bf16_hi(af[h]), v0 + 2 * h + 1);
-          } else {
-            visit(__uint_as_float(aq[h]), __uint_as_float(ap[h]), __uint_as_float(af[h]), v0 + h);
+        for (int e = 0; e < 3; ++e) {
+          const uint32_t ww[4] = {w[e][q].x, w[e][q].y, w[e][q].z, w[e][q].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            if constexpr (DT == 1) {
+              x[e][2 * h] = bf16_lo(ww[h]);
+              x[e][2 * h + 1] = bf16_hi(ww[h]);
+            } else {
+              x[e][h] = __uint_as_float(ww[h]);
+            }
           }
         }
+        const int v0 = e0 + vi * VPE;
+#pragma unroll
+        for (int g = 0; g < VPE; g += 4) visit4(&x[0][g], &x[1][g], &x[2][g], v0 + g);
         flush();
+      }
+    };
+    if (nfull > 0) {
+      u32x4 wa[3][kBatch], wb[3][kBatch];
+      fetch(0, wa);
+      for (int i0 = 0; i0 < kVecPerThread && i0 * kThreads < nfull; i0 += 2 * kBatch) {
+        fetch(i0 + kBatch, wb);
+        use(i0, wa);
+        if ((i0 + kBatch) >= kVecPerThread || (i0 + kBatch) * kThreads >= nfull) break;
+        fetch(i0 + 2 * kBatch, wa);
+        use(i0 + kBatch, wb);
       }
     }
     const int v = e0 + nfull * VPE + tid;
@@ -346,6 +401,20 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, bool h
     }
   }
   flush();
+}
+
+// pair_scan with the stages present at this position (stage 0 needs a draft
+// row, j < k; stage 1 the hierarchy); at least one of them is.
+template <int DT, class List>
+__device__ inline void pair_scan_any(const char* const* base, int e0, int e1, bool has0,
+                                     bool has1, float s, const PairShared& sh, List& L0, List& L1,
+                                     double& B0, double& B1) {
+  if (has0 && has1)
+    pair_scan<DT, true, true>(base, e0, e1, s, sh, L0, L1, B0, B1);
+  else if (has1)
+    pair_scan<DT, false, true>(base, e0, e1, s, sh, L0, L1, B0, B1);
+  else
+    pair_scan<DT, true, false>(base, e0, e1, s, sh, L0, L1, B0, B1);
 }
 
 // One workgroup per (sequence b, position j, chunk).  Rows: q = exit 0 row j
@@ -394,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void pair_kernel(ByArgs a) {
   L0.init();
   L1.init();
   double B0 = 0.0, B1 = 0.0;
-  pair_scan<DT>(base, e0, e1, has0, has1, s, sh, L0, L1, B0, B1);
+  pair_scan_any<DT>(base, e0, e1, has0, has1, s, sh, L0, L1, B0, B1);
 
   const int64_t stride_s = static_cast<int64_t>(a.k + 1) * a.nc;
   PairPart* out0 = a.pair + (static_cast<int64_t>(b) * 2 * (a.k + 1) + j) * a.nc + chunk;
@@ -417,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void pair_kernel(ByArgs a) {
   X0.init();
   X1.init();
   double D0 = 0.0, D1 = 0.0;
-  pair_scan<DT>(base, e0, e1, has0, has1, s, sh, X0, X1, D0, D1);
+  pair_scan_any<DT>(base, e0, e1, has0, has1, s, sh, X0, X1, D0, D1);
   if (has0) block_top(X0, a.top_m, out0, sh);
   if (has1) block_top(X1, a.top_m, out1, sh);
 }
