@@ -48,7 +48,15 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
   const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
   const int e0 = chunk * CE;
   double T;
-  const Partial p = chunk_stats<DT, ENT>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+  // the entropy sums first without the clamp; a chunk holding a -inf logit
+  // (T comes out NaN in every thread) is scanned again with it
+  Partial p = chunk_stats<DT, ENT, !ENT>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+  if constexpr (ENT) {
+    if (T != T) {
+      __syncthreads();   // lds is read by the reduction just finished
+      p = chunk_stats<DT, true, true>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+    }
+  }
   if (tid == 0) {
     a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
     if constexpr (ENT) a.tpart[static_cast<int64_t>(row) * a.nc + chunk] = T;

@@ -129,8 +129,12 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 
 
 // Partial statistics of elements [e0, e1) of one row (e1 - e0 <= one chunk).
 // Called by the whole workgroup (it contains barriers).  With ENT, T_out
-// receives the chunk's T (0 for a greedy row).
-template <int DT, bool ENT>
+// receives the chunk's T (0 for a greedy row).  CLAMP (with ENT): the vector
+// loop clamps the exponent of each T term, so that an element of weight 0
+// (l = -inf) adds 0; without it such an element makes T NaN, which the caller
+// detects and answers with a clamped rescan (identical otherwise: the clamp
+// only moves exponents below -1e30).
+template <int DT, bool ENT, bool CLAMP = true>
 __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds,
                                double& T_out) {
   constexpr int VPE = DT == 1 ? 8 : 4;
@@ -194,7 +198,7 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
         for (int q = 0; q < VPE; ++q) {
           const float y = fmaf(x[q], s, nc_);
           t[q] = __builtin_amdgcn_exp2f(y);
-          if constexpr (ENT) ty = fmaf(t[q], fmaxf(y, -1e30f), ty);
+          if constexpr (ENT) ty = fmaf(t[q], CLAMP ? fmaxf(y, -1e30f) : y, ty);
         }
         // pairwise within the vector, fp64 across vectors
 #pragma unroll
@@ -202,7 +206,9 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
 #pragma unroll
           for (int q = 0; q < w; ++q) t[q] += t[q + w];
         S += static_cast<double>(t[0]);
-        if constexpr (ENT) T += static_cast<double>(ty);
+        // (a padding vector past the chunk adds nothing: its -inf pads would
+        // make an unclamped T NaN)
+        if constexpr (ENT) T += i * kThreads + tid < nfull ? static_cast<double>(ty) : 0.0;
       }
       if (has_tail) {
         const float y = fmaf(xt, s, nc_);

@@ -275,3 +275,50 @@ def test_tied_and_clustered_residuals(sv):
     assert list(tok[0, 0, 0]) == list(range(8, 16))
     assert list(tok[1, 0, 0]) == [0, 1, 2, 4, 5, 6, 7, 8]
     assert list(tok[2, 0, 1][:4]) == [4001, 4003, 4002, 4000]
+
+
+def _mask(x, gen, frac, narrow_rows):
+    """Masked vocabulary: a fraction `frac` of every row's logits set to -inf,
+    and in `narrow_rows` (row indices of the flattened [B * n] rows) all but
+    three entries.  In place; x is a CPU tensor [B, n, V]."""
+    B, n, V = x.shape
+    m = torch.rand((B, n, V), generator=gen) < frac
+    flat = m.view(B * n, V)
+    for r in narrow_rows:
+        keep = torch.randperm(V, generator=gen)[:3]
+        flat[r] = True
+        flat[r, keep] = False
+    x[m] = float("-inf")
+
+
+@pytest.mark.parametrize("kind,dt", [("single", "bf16"), ("hier", "f32"), ("hier", "bf16")])
+def test_masked_vocabulary(sv, kind, dt):
+    """-inf logits (a masked vocabulary): the row statistics, the decisions,
+    the draws, the entropies (the stream's unclamped T sums turn NaN on such
+    chunks and are taken again with the clamp) and the outcome export all
+    against the oracle.  Drafted tokens are drawn where q > 0 by the workload
+    before masking, so some fall on masked entries (q(x) = 0 or p(x) = 0)."""
+    B, k, V = 6, 4, 9001
+    gen = torch.Generator().manual_seed(91)
+    if kind == "single":
+        w = workloads.make_single(B, k, V, dtype=dt, temps=(1.0, 0.7), seed=(66, V))
+        _mask(w["draft_logits"], gen, 0.3, [1, 7])
+        _mask(w["target_logits"], gen, 0.3, [2, 8])
+        keys = ("accept_len", "out_tokens", "num_emitted", "num_drop")
+        ref = P.oracle_single(w, 5, 6)
+    else:
+        w = workloads.make_hier(B, k, V, dtype=dt, temps=(1.0, 0.7), window=4, seed=(67, V),
+                                ctx=(16, 64))
+        _mask(w["ld_logits"], gen, 0.3, [1])
+        _mask(w["li_logits"], gen, 0.3, [3, 9])
+        _mask(w["lf_logits"], gen, 0.3, [4])
+        keys = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop")
+        ref = P.oracle_hier(w, 5, 6, 4)
+    out = _run(sv, w, 5, 6, entropy=True, outcome=True, top_m=4, diag=True)
+    torch.cuda.synchronize()
+    report = {}
+    P.compare(out, ref, keys, range(B), dt == "bf16", report)
+    worst = check_entropy(out["entropy"].cpu().numpy(), w)
+    n = check_outcome(out, w, 4)
+    print(f"masked {kind} {dt}: {report}, entropy worst rel {worst:.2e}, {n} positions")
+    assert report["compared"] >= B - 1
