@@ -137,11 +137,8 @@ struct TopList {
 };
 
 // Residuals and probabilities here are non-negative floats (or +0), whose
-// bit patterns order like unsigned integers: min and max run as integer
-// operations, exact and free of the float min/max NaN handling.
-__device__ __forceinline__ float umaxf(float a, float b) {
-  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
-}
+// bit patterns order like unsigned integers: min runs as an integer
+// operation, exact and free of the float min NaN handling.
 __device__ __forceinline__ float uminf(float a, float b) {
   return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
 }
