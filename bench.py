@@ -129,10 +129,11 @@ def _per_dispatch(rows, counter, ids):
 
 def _ids(rows):
     """Dispatch ids of the row-statistics kernel, and of the calibration copy
-    (the last three dispatches of the process)."""
+    (the last three kernel dispatches of the process; the runtime's own
+    buffer-copy kernels that read results back to the host come after it)."""
     names = {i: n for i, n, _, _ in rows}
     stats = {i for i, n in names.items() if "rowstats_kernel<1, false>" in n}
-    last = sorted(names)[-3:]
+    last = sorted(i for i, n in names.items() if not n.startswith("__amd_rocclr_"))[-3:]
     if len({names[i] for i in last}) != 1 or any(i in stats for i in last):
         raise SystemExit("the last three dispatches are not the calibration copy")
     return stats, set(last)
