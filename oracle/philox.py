@@ -15,7 +15,8 @@ constants (K0 += C0, K1 += C1 mod 2^W).  Philox4x32-10 is W = 32 with ten rounds
 The same code serves W = 32 (uint64 NumPy arithmetic, products are exact below
 2^64) and W = 64 (Python-int object arrays, exact 128-bit products).  The W = 64
 instantiation exists only so that the round structure can be pinned against a
-library (``numpy.random.Philox`` is Philox4x64-10).
+library (``numpy.random.Philox`` is Philox4x64-10); the W = 32 instance is
+pinned by the authors' published known-answer vectors.
 
 Uniform mapping used by the verifier (a reading, the pages fix none): a block is
 drawn per (position j, sequence b, stage s, call offset), counter

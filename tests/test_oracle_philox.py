@@ -3,9 +3,11 @@
 The round structure and key schedule are shared by all Philox-4xW widths; the
 W = 64 instantiation is checked bit for bit against ``numpy.random.Philox``
 (Philox4x64-10, a library routine), which pins the word order, the products,
-the xors and the key bumps.  The W = 32 constants are the published ones (no
-library in the CPU container exposes Philox4x32).  Statistical checks cover the
-24-bit uniforms the verifier takes from it.
+the xors and the key bumps.  The W = 32 instance is pinned by the known-answer
+vectors that the generator's authors publish with their Random123 library
+(philox4x32, 10 rounds: zero counter and key, all-ones counter and key, and the
+digits-of-pi counter and key).  Statistical checks cover the 24-bit uniforms
+the verifier takes from it.
 """
 
 import numpy as np
@@ -31,6 +33,23 @@ def _ours64(counter, key):
 def _add(counter, d):
     c0 = counter[0] + d
     return (c0 & (2 ** 64 - 1), counter[1] + (c0 >> 64), counter[2], counter[3])
+
+
+# (counter, key, output) of Philox4x32-10, Random123 known-answer vectors
+_KAT_4x32 = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+def test_philox4x32_known_answers():
+    for counter, key, want in _KAT_4x32:
+        w = philox.philox4(counter, key, philox.PHILOX_4x32, 10)
+        assert tuple(int(np.asarray(x).item()) for x in w) == want
 
 
 def test_round_structure_against_numpy_philox4x64():
