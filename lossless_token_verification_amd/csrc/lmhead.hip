@@ -13,10 +13,11 @@
 //
 // Tiling (512 threads, 2 x 4 wavefronts of 96 x 64 outputs each): both
 // operands are K-contiguous (hidden states [rows, d], head [V, d]), so each
-// 64-element K step of the A and W tiles is copied to LDS with 16-byte loads
-// and stores, and every MFMA operand is one 16-byte LDS read per lane.  The
-// global loads of a step are issued two steps ahead (two register stages, two
-// LDS buffers, one barrier per step).  Workgroup i runs on XCD i % 8; the M
+// 64-element K step of the A and W tiles is loaded from global memory straight
+// into LDS (16-byte direct loads, no register stage, rows of 128 bytes with an
+// XOR-permuted vector order), and every MFMA operand is one 16-byte LDS read
+// per lane.  The direct loads of a step are issued one step ahead into the
+// other of two LDS buffers (one barrier per step).  Workgroup i runs on XCD i % 8; the M
 // tiles of one vocabulary tile are consecutive on one XCD, so the W tile is
 // fetched from HBM once and served to the other M tiles from that XCD's L2.
 #include <algorithm>
@@ -39,17 +40,17 @@ struct GemmCfg {
   static constexpr int FM = MT / (WM * 32), FN = NT / (WN * 32);
   static constexpr int GT = WM * WN * kWave;          // threads per workgroup
   static constexpr int KT = KT_;
-  static constexpr int LROW = KT + 8;                 // bf16 per LDS row (16-byte pad)
   static constexpr int VPR = KT / 8;                  // 16-byte vectors per tile row
-  static constexpr int A_PER = MT * VPR / GT;         // A vectors each thread copies per step
-  static constexpr int B_PER = NT * VPR / GT;
+  static constexpr int WAVES = WM * WN;
+  // A direct load of one wavefront fills 1 KiB of LDS: 64 lanes x 16 bytes,
+  // KROWS whole tile rows.
+  static constexpr int KROWS = kWave / VPR;
+  static constexpr int A_LD = MT / KROWS / WAVES;     // direct loads per wavefront per step
+  static constexpr int B_LD = NT / KROWS / WAVES;
   static_assert(FM * WM * 32 == MT && FN * WN * 32 == NT, "tile shape");
-  static_assert(MT * VPR % GT == 0 && NT * VPR % GT == 0, "copy slots");
+  static_assert(VPR == 8, "one 128-byte LDS row per tile row (the swizzle spans 8 vectors)");
+  static_assert(A_LD * KROWS * WAVES == MT && B_LD * KROWS * WAVES == NT, "copy slots");
 
-  struct Tiles {
-    alignas(16) uint16_t a[2][MT * LROW];
-    alignas(16) uint16_t b[2][NT * LROW];
-  };
   struct Epi {
     float m[WN][MT];
     int i[WN][MT];
@@ -59,11 +60,14 @@ struct GemmCfg {
     float rmax[MT];
     int ridx[MT];
   };
-  union Shared {
-    Tiles t;
-    Epi e;            // used after the last K step
-  };
 };
+
+// LDS position (16-byte vector) of vector kv of tile row r: rows are 128
+// bytes, unpadded, and the vectors of a row are permuted by (r / 2) mod 8, so
+// that the 16 rows one MFMA operand read takes at the same kv fall on 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int kv) { return r * 8 + (kv ^ ((r >> 1) & 7)); }
+
 // statistics over all B(2k+1) rows; recompute of the 2B stopped rows
 using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
 using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
@@ -120,11 +124,14 @@ __device__ __forceinline__ void row_meta(const GemmArgs& a, int g, int& b, int& 
 template <class C, bool ROWS>
 __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
   constexpr int WN = C::WN, FM = C::FM, FN = C::FN, GT = C::GT;
-  constexpr int MT = C::MT, NT = C::NT, KT = C::KT, LROW = C::LROW, VPR = C::VPR;
-  constexpr int A_PER = C::A_PER, B_PER = C::B_PER;
-  __shared__ typename C::Shared sh;
-  typename C::Tiles& sm = sh.t;
-  typename C::Epi& ep = sh.e;
+  constexpr int MT = C::MT, NT = C::NT, KT = C::KT, VPR = C::VPR, KROWS = C::KROWS;
+  constexpr int A_LD = C::A_LD, B_LD = C::B_LD;
+  // two buffers of each operand, each its own LDS object: the compiler then
+  // knows a direct load into one buffer cannot change the other, and does not
+  // wait for it before reading the other
+  __shared__ __attribute__((aligned(1024))) uint16_t sa0[MT * KT], sa1[MT * KT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb0[NT * KT], sb1[NT * KT];
+  __shared__ typename C::Epi ep;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / WN, wn = wave - wm * WN;
   const int nM = (a.M + MT - 1) / MT;
@@ -134,42 +141,47 @@ __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
   if (ntile >= a.n_tiles) return;   // padding of the grid to a multiple of 8 tiles
   const int m0 = mtile * MT, n0 = ntile * NT;
 
-  // Copy slots of this thread: tile row v / VPR, 16-byte vector v % VPR.
-  // Rows past the matrix read a valid row instead (clamped, or row 0 for a
-  // skipped recompute row): each output depends only on its own A and W rows,
-  // and the epilogue never reports those rows or columns.
-  const uint16_t* ap[A_PER];
-  const uint16_t* bp[B_PER];
-  int aoff[A_PER], boff[B_PER];
+  // Direct loads (global memory to LDS, no register stage): load i of this
+  // wavefront fills tile rows (wave + i * WAVES) * KROWS .. + KROWS - 1, lane l
+  // the LDS vector l of that 1 KiB, which holds vector kv of row r with
+  // swz(r, kv) = that position.  Rows past the matrix read a valid row instead
+  // (clamped, or row 0 for a skipped recompute row): each output depends only
+  // on its own A and W rows, and the epilogue never reports those rows or
+  // columns.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t* ap[A_LD];
+  const uint16_t* bp[B_LD];
+  {
+    const int rl = lane / VPR, slot = lane - rl * VPR;
 #pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
-    int g = min(m0 + r, a.M - 1);
-    if (ROWS) g = max(a.a_rows[g], 0);
-    ap[i] = a_row(a, g) + kv * 8;
-    aoff[i] = r * LROW + kv * 8;
+    for (int i = 0; i < A_LD; ++i) {
+      const int r = (wave_u + i * C::WAVES) * KROWS + rl;
+      const int kv = slot ^ ((r >> 1) & 7);
+      int g = min(m0 + r, a.M - 1);
+      if (ROWS) g = max(a.a_rows[g], 0);
+      ap[i] = a_row(a, g) + kv * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int r = (wave_u + i * C::WAVES) * KROWS + rl;
+      const int kv = slot ^ ((r >> 1) & 7);
+      const int n = min(n0 + r, a.V - 1);
+      bp[i] = a.w + static_cast<int64_t>(n) * a.ldw + kv * 8;
+    }
   }
+  typedef const void __attribute__((address_space(1)))* gptr_t;
+  typedef void __attribute__((address_space(3)))* lptr_t;
+  auto dload = [&](int k0, uint16_t* la, uint16_t* lb) {
 #pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int v = tid + i * GT, r = v / VPR, kv = v - r * VPR;
-    const int n = min(n0 + r, a.V - 1);
-    bp[i] = a.w + static_cast<int64_t>(n) * a.ldw + kv * 8;
-    boff[i] = r * LROW + kv * 8;
-  }
-  // Two register stages: the loads of step t land in stage t % 2 and are
-  // issued two steps before step t is copied to LDS.
-  u32x4 ra0[A_PER], rb0[B_PER], ra1[A_PER], rb1[B_PER];
-  auto gload = [&](int k0, u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER]) {
+    for (int i = 0; i < A_LD; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(ap[i] + k0),
+                                       (lptr_t)(la + (wave_u + i * C::WAVES) * 512),
+                                       16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k0);
-  };
-  auto lstore = [&](int buf, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER]) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) *reinterpret_cast<u32x4*>(&sm.a[buf][aoff[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) *reinterpret_cast<u32x4*>(&sm.b[buf][boff[i]]) = rb[i];
+    for (int i = 0; i < B_LD; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(bp[i] + k0),
+                                       (lptr_t)(lb + (wave_u + i * C::WAVES) * 512),
+                                       16, 0, 0);
   };
 
   f32x16 acc[FM][FN];
@@ -183,23 +195,22 @@ __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
   // a wavefront whose rows all lie past the matrix skips its MFMAs
   const bool active = m0 + wm * FM * 32 < a.M;
   const int nK = a.d / KT;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  auto compute = [&](int cur) {
+  const int frow = lane & 31, fh = lane >> 5;
+  auto compute = [&](const uint16_t* la, const uint16_t* lb) {
     if (!active) return;
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
+      const int kv = ks * 2 + fh;
       bf16x8 af[FM], bf[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * FM * 32 + fm * 32 + frow;
-        af[fm] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&sm.a[cur][r * LROW + ks * 16 + fk]));
+        af[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(la + swz(r, kv) * 8));
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int r = wn * FN * 32 + fn * 32 + frow;
-        bf[fn] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&sm.b[cur][r * LROW + ks * 16 + fk]));
+        bf[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lb + swz(r, kv) * 8));
       }
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -209,28 +220,22 @@ __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
     }
   };
-  // Step t: MFMAs on LDS buffer t % 2, then step t + 1 (register stage
-  // (t + 1) % 2) is copied to the other buffer and step t + 3 is loaded into
-  // that register stage.  Every load is unconditional (steps past the end
-  // reload the last one), so each copy waits only for its own stage's loads.
-  const int last = (nK - 1) * KT;
-  gload(0, ra0, rb0);
-  gload(min(KT, last), ra1, rb1);
-  lstore(0, ra0, rb0);
-  gload(min(2 * KT, last), ra0, rb0);
+  // Step t computes on buffer t % 2 while the direct loads of step t + 1 fill
+  // the other; the barrier closing each step also waits for those loads
+  // (__syncthreads waits for every outstanding memory operation of the
+  // wavefront, direct loads to LDS included).
+  dload(0, sa0, sb0);
   __syncthreads();
   int kt = 0;
   for (; kt + 2 <= nK; kt += 2) {
-    compute(0);
-    lstore(1, ra1, rb1);
-    gload(min((kt + 3) * KT, last), ra1, rb1);
+    dload((kt + 1) * KT, sa1, sb1);
+    compute(sa0, sb0);
     __syncthreads();
-    compute(1);
-    lstore(0, ra0, rb0);
-    gload(min((kt + 4) * KT, last), ra0, rb0);
+    if (kt + 2 < nK) dload((kt + 2) * KT, sa0, sb0);
+    compute(sa1, sb1);
     __syncthreads();
   }
-  if (kt < nK) compute(0);   // odd number of steps: the last one is in buffer 0
+  if (kt < nK) compute(sa0, sb0);   // odd number of steps: the last one is in buffer 0
 
   // Output element (fm, fn, q) of this lane: row wm*FM*32 + fm*32 + (q/4)*8 +
   // h*4 + q%4, column wn*FN*32 + fn*32 + c32 (h = lane / 32, c32 = lane % 32).
