@@ -143,7 +143,7 @@ struct MergeArgs {
   uint32_t* flags;
 };
 constexpr int kGemmMT = 192;   // rows per GEMM workgroup tile (statistics GEMM)
-constexpr int kGemmRowsMT = 128;  // rows per tile of the recompute GEMM (2B rows)
+constexpr int kGemmRowsMT = 256;  // rows per tile of the recompute GEMM (2B rows)
 constexpr int kGemmNT = 256;   // vocabulary entries per GEMM workgroup tile
 constexpr int kGemmWM = 2;     // wavefronts of a GEMM workgroup along rows
 constexpr int kGemmWN = 4;     // and along the vocabulary
