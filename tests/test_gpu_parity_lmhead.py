@@ -40,6 +40,8 @@ SMALL = [
     (3, 0, 64, 777, 0.3, (1.0,)),             # k = 0: bonus only
     (2, 63, 64, 300, 0.1, (1.0,)),            # k = 63
     (9, 5, 512, 20011, 0.05, (1.3,)),         # several M tiles, flat rows
+    # 2B = 280 recomputed rows: a second, partial recompute tile; 420 GEMM rows
+    (140, 1, 128, 3000, 0.2, (1.0, 0.0)),
 ]
 
 
