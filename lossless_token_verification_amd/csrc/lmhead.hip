@@ -123,7 +123,7 @@ __device__ __forceinline__ void row_meta(const GemmArgs& a, int g, int& b, int& 
 
 template <class C, bool ROWS>
 __global__ __launch_bounds__(C::GT) void lmhead_gemm(GemmArgs a) {
-  constexpr int WN = C::WN, FM = C::FM, FN = C::FN, GT = C::GT;
+  constexpr int WN = C::WN, FM = C::FM, FN = C::FN;
   constexpr int MT = C::MT, NT = C::NT, KT = C::KT, VPR = C::VPR, KROWS = C::KROWS;
   constexpr int A_LD = C::A_LD, B_LD = C::B_LD;
   // two buffers of each operand, each its own LDS object: the compiler then
