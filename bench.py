@@ -375,15 +375,20 @@ def bench_tentative(args):
     cap = k + 1
     lf = torch.zeros((B, cap + 1, V), dtype=torch.bfloat16, device=dev)
     lf[:, :k + 1] = w["lf_logits"]
+    # fresh logits every step, as in the headline bench (see --rotate)
+    copies = [(w["ld_logits"], w["li_logits"], lf)]
+    for _ in range(max(1, args.rotate) - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
     pend = sv.make_pending(B, cap, V, torch.bfloat16, dev)
     ws = sv.alloc_workspace(sv.tentative_workspace_bytes(B, k, V, torch.bfloat16, cap), dev)
     print("[bench] tentative workload ready", file=sys.stderr, flush=True)
 
     def step(i):
-        sv.spec_verify_tentative_round(w["ld_logits"], w["li_logits"], w["draft_tokens"],
+        ld, li, lf_i = copies[i % len(copies)]
+        sv.spec_verify_tentative_round(ld, li, w["draft_tokens"],
                                        w["temperature"], pend, seed=0, offset=2 * i,
                                        workspace=ws)
-        return sv.spec_verify_tentative_flush(lf, w["temperature"], pend, min_pending=1,
+        return sv.spec_verify_tentative_flush(lf_i, w["temperature"], pend, min_pending=1,
                                               seed=0, offset=2 * i, workspace=ws)
 
     for i in range(args.warmup):
@@ -409,7 +414,7 @@ def bench_tentative(args):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "hierarchical workload; one intermediate round, then a flush "
                                "of the pending tokens against the final exit",
-                   "B": B, "k": k, "V": V, "capacity": cap},
+                   "B": B, "k": k, "V": V, "capacity": cap, "input_copies": len(copies)},
         "approx_rows_read_per_step": rows_read,
     }
     print(json.dumps(line), flush=True)
@@ -424,6 +429,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="hier and tentative paths: copies of the logits the steps cycle through (1: every "
+                         "step reads the same buffers, whose re-read rows the next step can "
+                         "find in the memory-side cache)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a copy of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -495,9 +504,18 @@ def main():
                  outcome=args.byproducts in ("outcome", "all"))
     extra["top_m"] = 8 if extra["outcome"] else 0
 
+    # The steps cycle through `rotate` copies of the logits, as a serving loop
+    # verifies fresh logits every step: a step never finds the rows an earlier
+    # step read (the draws re-read up to 197 MB) in the 256 MB memory-side cache.
+    copies = [(w["ld_logits"], w["li_logits"], w["lf_logits"])]
+    for _ in range(max(1, args.rotate) - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
+    torch.cuda.synchronize()
+
     def step(i, events=None):
         # verification of both stages and the paged-KV rollback, one call
-        return call(w["ld_logits"], w["li_logits"], w["lf_logits"],
+        ld, li, lf = copies[i % len(copies)]
+        return call(ld, li, lf,
                     w["draft_tokens"], w["temperature"], table, lens,
                     block_size=w["block_size"], max_freed=1,
                     window=w["window"], seed=0, offset=i,
@@ -548,7 +566,8 @@ def main():
             "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "hierarchical verify + KV rollback, L_f rows read only up "
-                                   "to each sequence's stage-1 stop", "B": B, "k": k, "V": V},
+                                   "to each sequence's stage-1 stop", "B": B, "k": k, "V": V,
+                       "input_copies": len(copies)},
             "dense_bytes_per_step": launch_bytes, "read_bytes_per_step": read_bytes,
             "ld_li_rows_read": di_rows, "lf_rows_read": lf_rows,
             "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
@@ -569,7 +588,7 @@ def main():
             "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"hierarchical verify + KV rollback with {name}",
-                       "B": B, "k": k, "V": V},
+                       "B": B, "k": k, "V": V, "input_copies": len(copies)},
             "roofline": {"bound": "hbm",
                          "kernel": "rowstats_kernel<bf16, entropy>" if extra["entropy"]
                          else "rowstats_kernel<bf16>",
@@ -602,7 +621,7 @@ def main():
         "config": {"workload": "hierarchical verify + KV rollback, B=256 k=8 V=128256 bf16 "
                                "logits of L_d/L_i/L_f, window N_i=4, 16-slot KV blocks",
                    "B": B, "k": k, "V": V, "logits": "bf16", "window": w["window"],
-                   "block_size": w["block_size"]},
+                   "block_size": w["block_size"], "input_copies": len(copies)},
         "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_of_peak_step": round(step_gbps / HBM_PEAK_GBPS, 4),
