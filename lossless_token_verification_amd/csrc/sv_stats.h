@@ -5,8 +5,8 @@
 // nontemporal 128-bit loads up front, keeps the chunk in registers and reduces
 // it to partial softmax statistics:
 //   temperature > 0: c = round(max * s) and S = sum 2^(l * s - c), with
-//                    s = log2(e) / temperature (fp32 exponent; fp32 pairwise sum
-//                    of each thread's elements, fp64 across threads);
+//                    s = log2(e) / temperature (fp32 exponent; fp32 pairwise sums,
+//                    fp64 across vectors or, for plain bf16 rows, across threads);
 //   temperature = 0: the maximum and its lowest index (greedy decoding).
 // With ENT the sampled rows also give T = sum 2^(l * s - c) * (l * s - c),
 // which turns the row's merged (c, S, T) into its entropy ln S - ln 2 * T / S
@@ -189,6 +189,11 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
     } else if (!empty) {
       c = m * s;
       const float nc_ = -c;
+      // bf16 without entropy sums: the vector sums are added pairwise in fp32
+      // and converted once (fewer instructions at the same occupancy); the
+      // other variants, whose registers are tighter, add each vector's sum
+      // in fp64
+      constexpr bool kTree = DT == 1 && !ENT;
       float vsum[kVecPerThread];
 #pragma unroll
       for (int i = 0; i < kVecPerThread; ++i) {
@@ -202,22 +207,25 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
           t[q] = __builtin_amdgcn_exp2f(y);
           if constexpr (ENT) ty = fmaf(t[q], CLAMP ? fmaxf(y, -1e30f) : y, ty);
         }
-        // pairwise within the vector, then across the vectors below
+        // pairwise within the vector
 #pragma unroll
         for (int w = VPE / 2; w > 0; w >>= 1)
 #pragma unroll
           for (int q = 0; q < w; ++q) t[q] += t[q + w];
-        vsum[i] = t[0];
+        if constexpr (kTree) vsum[i] = t[0];
+        else S += static_cast<double>(t[0]);
         // (a padding vector past the chunk adds nothing: its -inf pads would
         // make an unclamped T NaN)
         if constexpr (ENT) T += i * kThreads + tid < nfull ? static_cast<double>(ty) : 0.0;
       }
-      // pairwise across the vectors too, one conversion to fp64
+      if constexpr (kTree) {
+        // pairwise across the vectors too, one conversion to fp64
 #pragma unroll
-      for (int w = kVecPerThread / 2; w > 0; w >>= 1)
+        for (int w = kVecPerThread / 2; w > 0; w >>= 1)
 #pragma unroll
-        for (int q = 0; q < w; ++q) vsum[q] += vsum[q + w];
-      S += static_cast<double>(vsum[0]);
+          for (int q = 0; q < w; ++q) vsum[q] += vsum[q + w];
+        S += static_cast<double>(vsum[0]);
+      }
       if (has_tail) {
         const float y = fmaf(xt, s, nc_);
         const float t = __builtin_amdgcn_exp2f(y);
