@@ -147,7 +147,9 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
   // flight while the current group is summed.  Every load of that loop is
   // unconditional (an index past the last whole tile reloads that tile, an
   // absent q row reads the p row), so the compiler waits only for the group it
-  // sums.  The ragged last tile, and misaligned rows, go element by element.
+  // sums; they are nontemporal, as in the statistics stream (the rows are read
+  // once more at most, by the one-tile rescan).  The ragged last tile, and
+  // misaligned rows, go element by element.
   template <int DT>
   __device__ __forceinline__ void tile_pass(const char* prow, const RowStat& ps, const char* qrow,
                             const RowStat& qs, bool has_q, float s, int V, int t_begin, int t_end,
@@ -182,8 +184,8 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
       for (int g = 0; g < G; ++g) {
         const int t = min(t0 + g, t_full - 1);
         const int64_t off = static_cast<int64_t>(t * TE + lane * VPE) * ES;
-        vp[g] = *reinterpret_cast<const u32x4*>(prow + off);
-        vq[g] = *reinterpret_cast<const u32x4*>(qsrc + off);
+        vp[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + off));
+        vq[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qsrc + off));
       }
     };
     auto reduce = [&](int t0, const u32x4 (&vp)[G], const u32x4 (&vq)[G]) {
@@ -275,9 +277,9 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
       for (int g = 0; g < G; ++g) {
         const int t = min(t0 + g, t_full - 1);
         const int64_t off = static_cast<int64_t>(t * TE + lane * VPE) * ES;
-        vi[g] = *reinterpret_cast<const u32x4*>(irow + off);
-        vf[g] = *reinterpret_cast<const u32x4*>(frow + off);
-        vd[g] = *reinterpret_cast<const u32x4*>(dsrc + off);
+        vi[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(irow + off));
+        vf[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(frow + off));
+        vd[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dsrc + off));
       }
     };
     auto reduce = [&](int t0, const u32x4 (&vi)[G], const u32x4 (&vd)[G], const u32x4 (&vf)[G]) {
