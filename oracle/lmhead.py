@@ -33,13 +33,13 @@ def lmhead_logits(h_raw, w_raw, chunk=4096):
 
 
 def spec_verify_lmhead_single(h_draft, h_target, w, draft_tokens, temperature, seed, offset,
-                              sequences=None):
+                              sequences=None, flips=None):
     """Batched single-stage verify through an LM head.
 
     h_draft [B, k, d] and h_target [B, k+1, d] hidden states, w [V, d] head,
     all uint16 bf16 bits; draft_tokens [B, k]; temperature [B] or None.
     Returns what ``verify.spec_verify_single`` returns on the head's logits
-    (sequences outside ``sequences`` are left at -1).
+    (sequences outside ``sequences`` are left at -1; ``flips`` as there).
     """
     B, k, d = h_draft.shape
     if h_target.shape != (B, k + 1, d):
@@ -55,4 +55,4 @@ def spec_verify_lmhead_single(h_draft, h_target, w, draft_tokens, temperature, s
         ld[seqs] = L[:nd].reshape(len(seqs), k, V)
         lt[seqs] = L[nd:].reshape(len(seqs), k + 1, V)
     return verify.spec_verify_single(ld, lt, draft_tokens, temperature, seed, offset,
-                                     sequences=seqs)
+                                     sequences=seqs, flips=flips)

@@ -36,7 +36,18 @@ def accept(u, p_x, q_x):
     return bool(u * q_x < p_x)
 
 
-def draw(weights, v):
+def _neighbour(weights, i, step):
+    """The nearest index before (step -1) or after (step +1) i with a positive
+    weight; i itself when there is none."""
+    j = i + step
+    while 0 <= j < len(weights):
+        if weights[j] > 0:
+            return j
+        j += step
+    return i
+
+
+def draw(weights, v, shift=0):
     """Inverse-CDF draw from a non-negative weight vector with uniform v in [0,1).
 
     C(i) = sum of weights[0..i] (sequential, index order), R = C(V-1).
@@ -44,6 +55,10 @@ def draw(weights, v):
     If rounding leaves no such i, the largest i with a positive weight is
     taken.  Returns (None, info) when R == 0.
     info = dict(R, t=v*R, c_lo=C(i-1), c_hi=C(i)) for the parity exemptions.
+
+    ``shift`` = -1 / +1 takes, instead, the nearest index before / after that
+    one with a positive weight (the other side of a CDF boundary the threshold
+    lies next to); info still describes the inverse-CDF pick.
     """
     C = np.cumsum(weights)
     R = C[-1]
@@ -56,7 +71,10 @@ def draw(weights, v):
     else:
         i = int(np.nonzero(weights > 0)[0][-1])
     c_lo = C[i - 1] if i > 0 else 0 * R
-    return i, dict(R=R, t=t, c_lo=c_lo, c_hi=C[i])
+    info = dict(R=R, t=t, c_lo=c_lo, c_hi=C[i])
+    if shift:
+        i = _neighbour(weights, i, shift)
+    return i, info
 
 
 def residual(P, Q):
@@ -64,12 +82,19 @@ def residual(P, Q):
     return np.maximum(P - Q, 0 * P[0])
 
 
-def verify_chain(Q_rows, P_rows, tokens, us, vs, bonus_row=None, window=None):
+def verify_chain(Q_rows, P_rows, tokens, us, vs, bonus_row=None, window=None, flip=None):
     """Verify drafted ``tokens`` (length n) against (Q_j, P_j), j < n.
 
     Positions are visited in windows of ``window`` consecutive positions (all of
     them at once when None); within the call the result does not depend on the
     window size -- a window only groups tests.
+
+    ``flip`` takes one decision the other way, which gives the outcome an
+    implementation that rounds differently reaches at a near tie:
+    ("test", j) inverts the accept test at position j; ("draw", -1) or
+    ("draw", +1) takes the nearest token before or after the inverse-CDF pick
+    that has a positive weight; ("draw", "p") draws from P_a as the R = 0
+    fallback does.  None: the rule as stated.
 
     Returns (a, emitted, info):
       a       number of accepted leading tokens (first rejection, else n);
@@ -81,6 +106,8 @@ def verify_chain(Q_rows, P_rows, tokens, us, vs, bonus_row=None, window=None):
     if window is not None and int(window) < 1:
         raise ValueError("window must be >= 1")
     w = max(n, 1) if window is None else int(window)
+    flip_test = flip[1] if flip is not None and flip[0] == "test" else None
+    flip_draw = flip[1] if flip is not None and flip[0] == "draw" else None
     tests = []
     a = n
     start = 0
@@ -89,19 +116,27 @@ def verify_chain(Q_rows, P_rows, tokens, us, vs, bonus_row=None, window=None):
             p_x = prob_at(P_rows[j], tokens[j])
             q_x = prob_at(Q_rows[j], tokens[j])
             tests.append((us[j], p_x, q_x))
-            if not accept(us[j], p_x, q_x):
+            ok = accept(us[j], p_x, q_x)
+            if j == flip_test:
+                ok = not ok
+            if not ok:
                 a = j
                 break
         start += w
     emitted = [int(t) for t in tokens[:a]]
     draw_info = None
+    shift = flip_draw if flip_draw in (-1, 1) else 0
     if a < n:
-        y, draw_info = draw(residual(P_rows[a], Q_rows[a]), vs[a])
-        if y is None:
+        if flip_draw == "p":
             y, draw_info = draw(P_rows[a], vs[a])
             draw_info["fallback"] = True
+        else:
+            y, draw_info = draw(residual(P_rows[a], Q_rows[a]), vs[a], shift)
+            if y is None:
+                y, draw_info = draw(P_rows[a], vs[a], shift)
+                draw_info["fallback"] = True
         emitted.append(y)
     elif bonus_row is not None:
-        y, draw_info = draw(bonus_row, vs[n])
+        y, draw_info = draw(bonus_row, vs[n], shift)
         emitted.append(y)
     return a, emitted, dict(tests=tests, draw=draw_info)

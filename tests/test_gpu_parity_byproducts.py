@@ -226,10 +226,10 @@ def test_identical_rows_accept_everything(sv):
     assert (out["residual_tokens"].cpu().numpy()[:, 0, :4] == -1).all()
 
 
-def test_rollback_call_matches_and_full_size(sv):
+@pytest.fixture(scope="module")
+def full_size(sv):
     """The benchmarked call (hierarchy + KV rollback) at B=256 k=8 V=128256 bf16
-    with every by-product: sampled sequences against the oracle, and the
-    verification outputs equal those of the same call without by-products."""
+    with every by-product, and the same call without them."""
     w = workloads.make("hier", 0, device=DEV)
     kw = dict(block_size=w["block_size"], max_freed=1, window=w["window"])
     t1, l1 = w["block_table"].clone(), w["seq_lens"].clone()
@@ -240,18 +240,38 @@ def test_rollback_call_matches_and_full_size(sv):
     base = sv.spec_verify_hier_rollback(w["ld_logits"], w["li_logits"], w["lf_logits"],
                                         w["draft_tokens"], w["temperature"], t2, l2, **kw)
     torch.cuda.synchronize()
+    host = {kk: (v.cpu() if torch.is_tensor(v) else v) for kk, v in out.items()}
+    return dict(w=P._host(w), out=host, base=base, kv=(t1, l1, t2, l2), raw_out=out)
+
+
+def test_full_size_byproducts_leave_outputs_unchanged(full_size):
+    """Requesting the by-products changes no verification output or KV state."""
+    out, base = full_size["raw_out"], full_size["base"]
     for key in ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop",
                 "freed_blocks", "num_freed"):
         assert torch.equal(out[key], base[key]), key
+    t1, l1, t2, l2 = full_size["kv"]
     assert torch.equal(t1, t2) and torch.equal(l1, l2)
-    wc = {kk: (v.cpu() if torch.is_tensor(v) else v) for kk, v in w.items()}
-    seqs = sorted(np.random.default_rng(5).choice(w["B"], size=6, replace=False).tolist())
-    worst = check_entropy(out["entropy"].cpu().numpy(), wc, sequences=seqs)
-    n = check_outcome(out, wc, 8, sequences=seqs)
-    # every entry is finite where defined
-    ent = out["entropy"].cpu().numpy()
+
+
+def test_full_size_entropies(full_size):
+    """Every row entropy of every sequence against the oracle."""
+    w, out = full_size["w"], full_size["out"]
+    worst = check_entropy(out["entropy"].numpy(), w)
+    ent = out["entropy"].numpy()
     assert np.isfinite(ent).all() and (ent >= 0).all() and (ent <= np.log(w["V"]) + 1e-3).all()
-    print(f"full size: entropy worst rel {worst:.2e}, {n} positions")
+    print(f"full size: entropy worst rel {worst:.2e}")
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_full_size_outcome_export(full_size, half):
+    """The outcome export (beta, top 8 residual tokens) of every tested
+    position of every sequence against the oracle, in two halves of the batch."""
+    w, out = full_size["w"], full_size["out"]
+    B = w["B"]
+    seqs = list(range(half * B // 2, (half + 1) * B // 2))
+    n = check_outcome(out, w, 8, sequences=seqs)
+    print(f"full size: outcome export of {n} positions (sequences {seqs[0]}..{seqs[-1]})")
 
 
 def test_tied_and_clustered_residuals(sv):
@@ -317,7 +337,8 @@ def test_masked_vocabulary(sv, kind, dt):
     out = _run(sv, w, 5, 6, entropy=True, outcome=True, top_m=4, diag=True)
     torch.cuda.synchronize()
     report = {}
-    P.compare(out, ref, keys, range(B), dt == "bf16", report)
+    alt = P.alt_single(w, 5, 6) if kind == "single" else P.alt_hier(w, 5, 6, 4)
+    P.compare(out, ref, keys, range(B), dt == "bf16", report, alt=alt)
     worst = check_entropy(out["entropy"].cpu().numpy(), w)
     n = check_outcome(out, w, 4)
     print(f"masked {kind} {dt}: {report}, entropy worst rel {worst:.2e}, {n} positions")

@@ -55,10 +55,9 @@ def test_lmhead_small_parity(sv, case):
         out = _run(sv, w, seed=trial + 1, offset=trial * 5)
         torch.cuda.synchronize()
         ref = P.oracle_lmhead(w, trial + 1, trial * 5)
-        P.compare(out, ref, KEYS, range(B), True, report)
+        P.compare(out, ref, KEYS, range(B), True, report, alt=P.alt_lmhead(w, trial + 1, trial * 5))
     print(f"lmhead {case}: {report}")
-    total = report["compared"] + report["exempt"]
-    assert report["exempt"] <= max(1, total // 5), report
+    P.check_floor(report, 0.75)
 
 
 def test_lmhead_identical_exits_accept_all(sv):
@@ -120,7 +119,7 @@ def test_lmhead_host_validation(sv):
 def test_full_size_lmhead(sv):
     """B=128, k=4, d=4096, V=128256 (the fused LM-head workload), in the
     benchmark's launch configuration: every sequence's outputs are
-    well-formed, sampled sequences match the oracle."""
+    well-formed and every sequence is compared with the oracle."""
     w = workloads.make("lmhead", 0, device=DEV)
     out = _run(sv, w, 0, 0)
     torch.cuda.synchronize()
@@ -130,10 +129,9 @@ def test_full_size_lmhead(sv):
     toks = out["out_tokens"].cpu().numpy()
     assert ((a >= 0) & (a <= k)).all() and (ne == a + 1).all()
     assert ((toks >= 0) | (np.arange(k + 1)[None] >= ne[:, None])).all() and toks.max() < V
-    wc = {kk: (v.cpu() if torch.is_tensor(v) else v) for kk, v in w.items()}
-    seqs = sorted(np.random.default_rng(5).choice(B, size=12, replace=False).tolist())
-    ref = P.oracle_lmhead(wc, 0, 0, sequences=seqs)
+    wc = P._host(w)
+    ref = P.oracle_lmhead(wc, 0, 0)
     report = {}
-    P.compare(out, ref, KEYS, seqs, True, report)
+    P.compare(out, ref, KEYS, range(B), True, report, alt=P.alt_lmhead(wc, 0, 0))
     print("lmhead full size:", report)
-    assert report["compared"] >= 6, report
+    P.check_floor(report, 0.75)

@@ -68,8 +68,8 @@ def test_single_sweep(sv, cfg):
     torch.cuda.synchronize()
     ref = P.oracle_single(w, i, 3 * i)
     report = {}
-    P.compare(out, ref, SINGLE_KEYS, range(B), dt == "bf16", report)
-    assert report["exempt"] <= max(1, (report["compared"] + report["exempt"]) // 10), report
+    P.compare(out, ref, SINGLE_KEYS, range(B), dt == "bf16", report, alt=P.alt_single(w, i, 3 * i))
+    P.check_floor(report, 0.9)
 
 
 @pytest.mark.parametrize("cfg", _configs(12, 2025), ids=lambda c: f"s{c[0]}B{c[1]}k{c[2]}V{c[3]}{c[4]}w{c[7]}")
@@ -85,7 +85,8 @@ def test_hier_sweep(sv, cfg):
     torch.cuda.synchronize()
     ref = P.oracle_hier(w, i, 5 * i, window)
     report = {}
-    P.compare(out, ref, HIER_KEYS, range(B), dt == "bf16", report)
+    P.compare(out, ref, HIER_KEYS, range(B), dt == "bf16", report,
+              alt=P.alt_hier(w, i, 5 * i, window))
     # long chains over close L_i / L_f rows leave small stage-2 residual masses,
     # whose draws the exemption rule sets aside more often than single-stage ones
     print(f"hier sweep {cfg}: {report}")
@@ -106,5 +107,5 @@ def test_largest_vocabulary(sv, dt, k):
     torch.cuda.synchronize()
     ref = P.oracle_hier(w, 1, 2, 4)
     report = {}
-    P.compare(out, ref, HIER_KEYS, range(2), dt == "bf16", report)
+    P.compare(out, ref, HIER_KEYS, range(2), dt == "bf16", report, alt=P.alt_hier(w, 1, 2, 4))
     assert report["compared"] >= 1, report

@@ -171,7 +171,8 @@ def test_overflow_is_flagged_and_truncated(sv):
 
 def test_full_size_round_and_flush(sv):
     """B=256 k=8 V=128256 bf16: a round and a flush (min_pending 1) agree with
-    the one-call hierarchy's oracle on sampled sequences."""
+    the one-call hierarchy's oracle on every sequence (near ties: the oracle's
+    outcome or the one with that decision flipped)."""
     w = workloads.make("hier", 0, device=DEV)
     B, k, V = w["B"], w["k"], w["V"]
     cap = k + 1
@@ -181,19 +182,13 @@ def test_full_size_round_and_flush(sv):
     f = sv.spec_verify_tentative_flush(_pad_rows(w["lf_logits"], cap + 1), w["temperature"],
                                        pend, min_pending=1, seed=0, offset=0)
     torch.cuda.synchronize()
-    wc = {kk: (v.cpu() if torch.is_tensor(v) else v) for kk, v in w.items()}
-    seqs = sorted(np.random.default_rng(8).choice(B, size=12, replace=False).tolist())
-    ref = P.oracle_hier(wc, 0, 0, w["window"], sequences=seqs)
-    a1 = r["accept_len"].cpu().numpy()
-    a2 = f["accept_len"].cpu().numpy()
-    n = f["num_emitted"].cpu().numpy()
-    toks = f["out_tokens"].cpu().numpy()
-    compared = 0
-    for b in seqs:
-        if _near(ref["infos"][b]):
-            continue
-        compared += 1
-        assert a1[b] == ref["accept_len_inter"][b] and a2[b] == ref["accept_len_final"][b], b
-        assert toks[b, :n[b]].tolist() == ref["out_tokens"][b, :n[b]].tolist(), b
-    assert compared >= 10
+    wc = P._host(w)
+    ref = P.oracle_hier(wc, 0, 0, w["window"])
+    got = dict(accept_len_inter=r["accept_len"], accept_len_final=f["accept_len"],
+               out_tokens=f["out_tokens"][:, :k + 1], num_emitted=f["num_emitted"])
+    report = {}
+    P.compare(got, ref, ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted"),
+              range(B), True, report, alt=P.alt_hier(wc, 0, 0, w["window"]))
+    print("full size round + flush:", report)
+    P.check_floor(report, 0.9)
     assert (pend["count"].cpu() == 0).all()
