@@ -10,8 +10,11 @@ Bars (as the tests state them):
   the oracle's, or the oracle's with that one decision taken the other way
   (``alt``); only a tie whose other side is not one token (the R = 0 fallback)
   is left unchecked, and counted;
-* at least a stated fraction of the sequences (``check_floor``) is compared
-  bit for bit;
+* at least a stated fraction of the sequences (``check_floor``) is checked
+  against the oracle: bit for bit where the outcome is unique, against the
+  two allowed outcomes where it is a near tie (at V = 128256 the residual draw
+  often lands among tail tokens whose CDF steps are ~1e-6 wide, so ~10-20 %
+  of the headline's sequences are near ties of the CDF band);
 * p(x), q(x) of every tested position agree within PROB_ABS (fp32 logits) or
   PROB_REL relative (bf16 logits);
 * draw quantities (R, v*R, C(y-1), C(y)) of matching draws agree within
@@ -122,13 +125,16 @@ def compare(gpu, ref, keys, sequences, bf16, report=None, alt=None, ratio_eps=RA
 
 
 def check_floor(report, floor):
-    """At least ``floor`` of the sequences were compared bit for bit (with
-    fewer than 20 sequences in all, all but one)."""
+    """At least ``floor`` of the sequences were checked against the oracle:
+    compared bit for bit, or (near ties) found equal to one of the two
+    outcomes the tie allows; with fewer than 20 sequences in all, all but
+    one.  Unresolved ties (the R = 0 fallback) do not count."""
     total = report.get("compared", 0) + report.get("exempt", 0)
     assert total > 0, report
+    checked = total - report.get("exempt_unresolved", 0)
     need = floor * total if total >= 20 else total - 1
-    assert report["compared"] >= need, \
-        f"only {report['compared']} of {total} sequences compared (floor {floor}): {report}"
+    assert checked >= need, \
+        f"only {checked} of {total} sequences checked (floor {floor}): {report}"
 
 
 def _stage_infos(info):
