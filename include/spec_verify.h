@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 3
+#define SPEC_VERIFY_ABI_VERSION 4
 
 /* Status codes. */
 #define SV_OK 0
@@ -291,6 +291,32 @@ int32_t spec_verify_hier_rollback(const spec_verify_desc* desc, int32_t window,
                                   int32_t* freed_blocks, int32_t max_freed, int32_t* num_freed,
                                   void* workspace, size_t workspace_bytes,
                                   const spec_verify_diag* diag, void* hip_stream);
+
+/* spec_verify_hier_rollback without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing: its
+ * workspace is a static array of SV_NOALLOC_SCRATCH_BYTES in the library's
+ * device code, one per GPU, held until the process ends (the first call on a
+ * GPU looks up that GPU's copy; the GPU is hip_stream's, or the current device
+ * for the null stream).  Arguments, results and errors as for
+ * spec_verify_hier_rollback; a call whose workspace (spec_verify_workspace_bytes
+ * with num_exits = 3) exceeds SV_NOALLOC_SCRATCH_BYTES fails with
+ * SV_ERR_WORKSPACE and launches nothing.  Every call on one GPU uses the same
+ * array, which keeps the last call's contents (the call itself clears what must
+ * start at zero): calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined results. */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t spec_verify_hier_rollback_noalloc(const spec_verify_desc* desc, int32_t window,
+                                          const void* ld_logits, const void* li_logits,
+                                          const void* lf_logits, const int32_t* draft_tokens,
+                                          const float* temperature, int32_t* accept_len_inter,
+                                          int32_t* accept_len_final, int32_t* out_tokens,
+                                          int32_t* num_emitted, int32_t* num_drop,
+                                          int32_t max_blocks, int32_t block_size,
+                                          int32_t* block_table, int32_t* seq_lens,
+                                          int32_t* freed_blocks, int32_t max_freed,
+                                          int32_t* num_freed, const spec_verify_diag* diag,
+                                          void* hip_stream);
 
 /* Workspace bytes of spec_verify_lmhead_single (0 if desc or hidden is
  * invalid). */

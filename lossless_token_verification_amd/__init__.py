@@ -51,8 +51,10 @@ EXPORTED = (
     "spec_verify_device_status", "spec_verify_lmhead_workspace_bytes",
     "spec_verify_lmhead_single", "spec_verify_hier_rollback_lazy",
     "spec_verify_tentative_workspace_bytes", "spec_verify_tentative_round",
-    "spec_verify_tentative_flush",
+    "spec_verify_tentative_flush", "spec_verify_hier_rollback_noalloc",
 )
+# bytes of the static scratch of spec_verify_hier_rollback_noalloc (SV_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Desc(ctypes.Structure):
@@ -116,6 +118,10 @@ def library():
                                               ctypes.POINTER(Diag), P]
     lib.spec_verify_hier_rollback_lazy.restype = i32
     lib.spec_verify_hier_rollback_lazy.argtypes = lib.spec_verify_hier_rollback.argtypes
+    lib.spec_verify_hier_rollback_noalloc.restype = i32
+    lib.spec_verify_hier_rollback_noalloc.argtypes = [ctypes.POINTER(Desc), i32, P, P, P, P, P, P,
+                                                      P, P, P, P, i32, i32, P, P, P, i32, P,
+                                                      ctypes.POINTER(Diag), P]
     lib.kv_blocktable_truncate.restype = i32
     lib.kv_blocktable_truncate.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P]
     lib.spec_verify_device_status.restype = i32
@@ -404,7 +410,7 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
                               block_table, seq_lens, *, block_size, max_freed, window=4,
                               seed=0, offset=0, diag=False, workspace=None, events=None,
                               out=None, entropy=False, outcome=False, top_m=0, row_stats=False,
-                              _lazy=False):
+                              _lazy=False, _noalloc=False):
     """spec_verify_hier plus the paged-KV rollback of block_table / seq_lens
     (in place) in the same launches.  Returns the spec_verify_hier dict plus
     freed_blocks [B, max_freed] and num_freed [B].  ``out``: a dict returned
@@ -429,18 +435,29 @@ def spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, tem
     desc = make_desc(B, k, V, code, _common_stride([s0, s1, s2], V), seed, offset)
     need = lib.spec_verify_workspace_bytes(ctypes.byref(desc), 3)
     if out is None:
-        ws = workspace if workspace is not None else alloc_workspace(need, dev)
+        ws = None if _noalloc else (workspace if workspace is not None
+                                    else alloc_workspace(need, dev))
         out = dict(accept_len_inter=_int_out((B,), dev), accept_len_final=_int_out((B,), dev),
                    out_tokens=_int_out((B, k + 1), dev), num_emitted=_int_out((B,), dev),
                    num_drop=_int_out((B,), dev), freed_blocks=_int_out((B, max_freed), dev),
                    num_freed=_int_out((B,), dev), workspace=ws)
     else:
-        ws = out["workspace"]
+        ws = out.get("workspace")
         if tuple(out["out_tokens"].shape) != (B, k + 1) or \
                 tuple(out["freed_blocks"].shape) != (B, max_freed):
             raise ValueError("out buffers do not match this call's shapes")
     dg = _make_diag(diag, events, B, k, dev, out, B * (3 * k + 2), entropy, outcome, top_m,
                     row_stats)
+    if _noalloc:
+        _check(lib.spec_verify_hier_rollback_noalloc(
+            ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
+            _ptr(draft_tokens), _ptr(temperature), _ptr(out["accept_len_inter"]),
+            _ptr(out["accept_len_final"]), _ptr(out["out_tokens"]), _ptr(out["num_emitted"]),
+            _ptr(out["num_drop"]), int(max_blocks), int(block_size), _ptr(block_table),
+            _ptr(seq_lens), _ptr(out["freed_blocks"]) if max_freed > 0 else None,
+            int(max_freed), _ptr(out["num_freed"]),
+            ctypes.byref(dg) if dg is not None else None, _stream(dev)))
+        return out
     fn = lib.spec_verify_hier_rollback_lazy if _lazy else lib.spec_verify_hier_rollback
     _check(fn(
         ctypes.byref(desc), int(window), _ptr(ld_logits), _ptr(li_logits), _ptr(lf_logits),
@@ -459,6 +476,18 @@ def spec_verify_hier_rollback_lazy(ld_logits, li_logits, lf_logits, draft_tokens
     (rows 0..a1 of each sequence); bit-identical results."""
     return spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
                                      block_table, seq_lens, _lazy=True, **kw)
+
+
+def spec_verify_hier_rollback_noalloc(ld_logits, li_logits, lf_logits, draft_tokens,
+                                      temperature, block_table, seq_lens, **kw):
+    """spec_verify_hier_rollback whose workspace is the library's static
+    per-GPU scratch (the C call allocates nothing; calls that overlap on one
+    GPU race).  Takes no ``workspace``; the returned dict has workspace None."""
+    if kw.get("workspace") is not None:
+        raise ValueError("the no-allocation call takes no workspace")
+    kw.pop("workspace", None)
+    return spec_verify_hier_rollback(ld_logits, li_logits, lf_logits, draft_tokens, temperature,
+                                     block_table, seq_lens, _noalloc=True, **kw)
 
 
 def kv_blocktable_truncate(block_table, seq_lens, num_drop, block_size, max_freed):

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "spec_verify.h"
@@ -820,6 +821,57 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
 
 }  // namespace
 
+namespace {
+
+// Scratch of spec_verify_hier_rollback_noalloc, for callers that cannot
+// allocate: one array per GPU the library runs on, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it is
+// a stand-in, not a device address): the first call on a device looks up that
+// device's copy with hipGetSymbolAddress and keeps the address.
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the scratch array on the GPU that runs `st` (the current
+// device for the null stream).
+int32_t scratch_address(hipStream_t st, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  int dev = cur;
+  if (st) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(st, &d);
+    if (e != hipSuccess) return device_error(e, "hipStreamGetDevice");
+    dev = d;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SV_ERR_UNSUPPORTED, "device index " + std::to_string(dev) +
+                                        " beyond the scratch table of the no-allocation call");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return device_error(e, "hipSetDevice");
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess && r != hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return device_error(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SV_ERR_DEVICE, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t spec_verify_abi_version(void) { return SPEC_VERIFY_ABI_VERSION; }
@@ -933,6 +985,32 @@ int32_t spec_verify_lmhead_single(const spec_verify_desc* desc, int32_t hidden,
   return run_lmhead(desc, hidden, h_draft, h_target, w_vocab, draft_tokens, temperature,
                     accept_len, out_tokens, num_emitted, num_drop, packed_tokens, cu_offsets,
                     workspace, workspace_bytes, diag, hip_stream);
+}
+
+int32_t spec_verify_hier_rollback_noalloc(const spec_verify_desc* desc, int32_t window,
+                                          const void* ld_logits, const void* li_logits,
+                                          const void* lf_logits, const int32_t* draft_tokens,
+                                          const float* temperature, int32_t* accept_len_inter,
+                                          int32_t* accept_len_final, int32_t* out_tokens,
+                                          int32_t* num_emitted, int32_t* num_drop,
+                                          int32_t max_blocks, int32_t block_size,
+                                          int32_t* block_table, int32_t* seq_lens,
+                                          int32_t* freed_blocks, int32_t max_freed,
+                                          int32_t* num_freed, const spec_verify_diag* diag,
+                                          void* hip_stream) {
+  Plan p;
+  SV_TRY(make_plan(desc, 3, &p));
+  if (p.ws_bytes > kScratchBytes)
+    return fail(SV_ERR_WORKSPACE, "the call needs " + std::to_string(p.ws_bytes) +
+                                      " bytes of scratch; the no-allocation call holds " +
+                                      std::to_string(kScratchBytes));
+  void* ws = nullptr;
+  SV_TRY(scratch_address(static_cast<hipStream_t>(hip_stream), &ws));
+  const void* logits[3] = {ld_logits, li_logits, lf_logits};
+  KvRollback kv{max_blocks, block_size, max_freed, block_table, seq_lens, freed_blocks, num_freed};
+  return run_verify(desc, 3, window, logits, draft_tokens, temperature, accept_len_inter,
+                    accept_len_final, out_tokens, num_emitted, num_drop, nullptr, nullptr, ws,
+                    kScratchBytes, diag, hip_stream, &kv);
 }
 
 int32_t spec_verify_hier_rollback_lazy(const spec_verify_desc* desc, int32_t window,

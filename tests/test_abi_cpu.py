@@ -33,7 +33,7 @@ def sv():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert set(names) == set(sv.EXPORTED)
     lib = ctypes.CDLL(sv.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(sv):
 
 def test_version_and_status_strings(sv):
     lib = sv.library()
-    assert sv.abi_version() == 3
+    assert sv.abi_version() == 4
     for code, name in ((0, b"SV_OK"), (1, b"SV_ERR_INVALID_ARG"), (2, b"SV_ERR_UNSUPPORTED"),
                        (3, b"SV_ERR_MISALIGNED"), (4, b"SV_ERR_WORKSPACE"), (5, b"SV_ERR_DEVICE"),
                        (99, b"SV_ERR_UNKNOWN")):
@@ -251,3 +251,24 @@ def test_tentative_host_checks_without_gpu(sv):
     assert lib.spec_verify_tentative_flush(ctypes.byref(d), p, None, 4, ctypes.byref(pend), p,
                                            p, p, p, ctypes.c_void_p(0x10000), 1 << 30, None) == \
         sv.SV_ERR_MISALIGNED
+
+
+def test_noalloc_rejects_oversized_calls_on_the_host(sv):
+    """spec_verify_hier_rollback_noalloc refuses a call whose workspace exceeds
+    its static scratch before any HIP call (so it works here, without a GPU),
+    and reports the sizes."""
+    lib = sv.library()
+    # V = 2^20 bf16, k = 63: the workspace runs far past 16 MiB
+    d = sv.make_desc(256, 63, 1 << 20, sv.SV_DTYPE_BF16)
+    assert sv.workspace_bytes(256, 63, 1 << 20, sv.SV_DTYPE_BF16, 3) > sv.NOALLOC_SCRATCH_BYTES
+    z = ctypes.c_void_p(16)
+    st = lib.spec_verify_hier_rollback_noalloc(ctypes.byref(d), 4, z, z, z, z, None, z, z, z, z,
+                                               None, 8, 16, z, z, z, 1, z, None, None)
+    assert st == sv.SV_ERR_WORKSPACE
+    msg = lib.spec_verify_last_error().decode()
+    assert "scratch" in msg and str(sv.NOALLOC_SCRATCH_BYTES) in msg
+    # an invalid descriptor is reported as such, not as a size problem
+    bad = sv.make_desc(4, 3, 0, sv.SV_DTYPE_BF16)
+    assert lib.spec_verify_hier_rollback_noalloc(ctypes.byref(bad), 4, z, z, z, z, None, z, z, z,
+                                                 z, None, 8, 16, z, z, z, 1, z, None,
+                                                 None) == sv.SV_ERR_INVALID_ARG

@@ -49,7 +49,7 @@ HIER_KEYS = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted"
 
 
 def test_library_is_the_hip_build(sv):
-    assert sv.abi_version() == 3
+    assert sv.abi_version() == 4
     assert sv._lib is not None and sv.LIB_PATH.endswith("libspecverify.so")
 
 
