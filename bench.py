@@ -5,13 +5,22 @@ workload (B=256 sequences, k=8 drafted tokens, V=128256, bf16 logits of the
 three exits L_d, L_i, L_f, windows of N_i=4): spec_verify_hier_rollback (row
 statistics of every logit row, both verification stages, correction draws,
 and the rollback of the batch's paged-KV block tables).  Inputs are synthetic
-(seeded, see workloads/) and resident in HBM before the timed region.
+(seeded, see workloads/), drawn on the host and resident in HBM before the
+timed region.
+
+Before the counted warm-up steps the step runs back to back for --settle-ms
+(400 ms by default): in the first tens of milliseconds of sustained load the
+chip's power management holds the shader clock at 1.5-1.9 GHz before it
+settles at 2.2-2.3 GHz, and a serving loop that verifies continuously runs in
+the settled state.  The timed steps are full steps; the line reports each
+step's time distribution beside the total.
 
 Prints one JSON line: verified draft tokens/s (B*k per step), whole-step and
-row-statistics-kernel HBM bandwidth against the 8 TB/s peak, and the CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+row-statistics-kernel HBM bandwidth against the 8 TB/s peak, the oracle timed
+on the first timed step's inputs on this host's cores, and the parity of that
+step's outputs with the oracle's.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 300]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--settle-ms 400]
 """
 
 import argparse
@@ -42,49 +51,127 @@ def _rowstats_sha():
             h.update(f.read())
     return h.hexdigest()
 
-# --- CPU baseline (the oracle, on a bounded sample of the same workload) ----
+# --- the oracle leg: CPU baseline and parity of the timed outputs -----------
+#
+# The headline inputs are drawn on the host; worker processes are forked from
+# that state before any GPU call, so that they read the very logits, drafts and
+# temperatures the GPU consumes.  After the timed steps the oracle verifies the
+# first timed step's inputs (Philox offset 0): its wall time is the CPU
+# baseline, its outputs the reference the GPU's outputs are compared with.
 
 _CPU = {}
+HOST_SHARE = 16   # host CPU cores per GPU on the measured machine (the pool's size)
 
 
-def _cpu_worker(seqs):
+def _cpu_worker(job):
+    """Oracle of the hierarchical verify on a list of sequences; returns the
+    per-sequence outputs and infos (near-tie events need them)."""
     from oracle import verify
+    seqs, offset, flips = job
     w = _CPU
-    verify.spec_verify_hier(w["ld"], w["li"], w["lf"], w["tok"], w["temp"], 0, 0, 4,
-                            sequences=seqs)
-    return len(seqs)
+    r = verify.spec_verify_hier(w["ld"], w["li"], w["lf"], w["tok"], w["temp"], 0, offset, 4,
+                                sequences=seqs, flips=flips)
+    keys = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop")
+    return {b: ({k: r[k][b] for k in keys}, r["infos"][b]) for b in seqs}
 
 
-def cpu_baseline(sample_seqs, procs, min_seconds):
-    """Oracle wall time over ``procs`` forked worker processes (started before
-    any GPU use) on ``sample_seqs`` sequences shaped like the workload, passed
-    through the oracle again and again until ``min_seconds`` have gone by."""
-    import numpy as np
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_pool(host, procs):
+    """Fork ``procs`` oracle workers over the host inputs (before any GPU use)."""
+    _CPU.update(ld=workloads_raw(host["ld_logits"]), li=workloads_raw(host["li_logits"]),
+                lf=workloads_raw(host["lf_logits"]), tok=host["draft_tokens"].numpy(),
+                temp=host["temperature"].numpy())
+    return mp.get_context("fork").Pool(procs)
+
+
+def workloads_raw(t):
     import workloads
-    w = workloads.make_hier(sample_seqs, 8, 128256, seed=(3, 1000), ctx=(512, 4096))
-    _CPU.update(ld=workloads.to_numpy_raw(w["ld_logits"]), li=workloads.to_numpy_raw(w["li_logits"]),
-                lf=workloads.to_numpy_raw(w["lf_logits"]), tok=w["draft_tokens"].numpy(),
-                temp=w["temperature"].numpy())
-    del w
-    chunks = [list(c) for c in np.array_split(np.arange(sample_seqs), procs) if len(c)]
-    ctx = mp.get_context("fork")
-    with ctx.Pool(procs) as pool:
-        pool.map(_cpu_worker, [[0]] * procs)          # warm the workers
-        done, passes = 0, 0
+    return workloads.to_numpy_raw(t)
+
+
+def oracle_leg(pool, procs, B, k, offset, p1_seqs):
+    """The oracle on the first timed step's inputs: every sequence over the
+    pool (one untimed pass whose outputs are kept, then two timed passes), and
+    the first ``p1_seqs`` sequences in this process alone (P = 1).  Returns
+    (results {b: (outputs, info)}, cpu_baseline dict)."""
+    import numpy as np
+    chunks = [c.tolist() for c in np.array_split(np.arange(B), procs * 4) if len(c)]
+    res = {}
+    for part in pool.map(_cpu_worker, [(c, offset, None) for c in chunks]):
+        res.update(part)
+    times = []
+    for _ in range(2):
         t0 = time.perf_counter()
-        while True:
-            done += sum(pool.map(_cpu_worker, chunks))
-            passes += 1
-            dt = time.perf_counter() - t0
-            if dt >= min_seconds:
-                break
-    _CPU.clear()
-    return dict(value=done * 8 / dt, unit="verified draft tokens/s", cores=procs, kind="oracle",
-                sample=f"{passes} passes over {sample_seqs} sequences ({done} sequence "
-                       f"verifications) of the B=256 k=8 V=128256 bf16 hierarchical workload "
-                       f"(L_d, L_i, L_f logits, window 4), NumPy float64 oracle, one worker "
-                       f"process per core, {dt:.1f} s wall",
-                seconds=dt)
+        pool.map(_cpu_worker, [(c, offset, None) for c in chunks])
+        times.append(time.perf_counter() - t0)
+    t_pool = min(times)
+    t0 = time.perf_counter()
+    _cpu_worker((list(range(p1_seqs)), offset, None))
+    t_one = time.perf_counter() - t0
+    base = dict(value=round(B * k / t_pool, 2), unit="verified draft tokens/s", cores=procs,
+                kind="oracle",
+                sample=f"the first timed step's inputs (B={B} k={k} V=128256 bf16 L_d/L_i/L_f, "
+                       f"window 4, Philox offset {offset}): all {B} sequences over {procs} "
+                       f"forked processes, best of 2 passes ({t_pool:.2f} s); one process "
+                       f"over the first {p1_seqs} sequences ({t_one:.2f} s); NumPy float64",
+                p1_value=round(p1_seqs * k / t_one, 2), p1_sequences=p1_seqs,
+                cpu_model=_cpu_model(), os_cpu_count=os.cpu_count())
+    return res, base
+
+
+def parity_of_step(pool, res, gpu, offset, kv):
+    """Compares one step's GPU outputs with the oracle's: bit for bit where the
+    outcome is unique; at a near tie the GPU must give the oracle's outcome or
+    the one with that decision flipped (re-run by the oracle).  The rolled-back
+    block tables and lengths are compared with the oracle's rollback of the
+    GPU's own num_drop (bit for bit, every sequence)."""
+    import numpy as np
+    from oracle import blocktable, verify
+    keys = ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted", "num_drop")
+    g = {k: gpu[k].cpu().numpy() for k in keys}
+    exact = as_oracle = as_flip = unresolved = 0
+    mismatched = []
+    flips = {}
+    for b, (ref, info) in sorted(res.items()):
+        same = all(np.array_equal(g[k][b], ref[k]) for k in keys)
+        ev = verify.near_tie_event(info, 1e-5, 1e-6)
+        if ev is None:
+            exact += 1
+            if not same:
+                mismatched.append(b)
+        elif same:
+            as_oracle += 1
+        elif ev["flip"] is None:
+            unresolved += 1
+        else:
+            flips[b] = ev
+    if flips:
+        alt = {}
+        for part in pool.map(_cpu_worker, [([b], offset, {b: e}) for b, e in flips.items()]):
+            alt.update(part)
+        for b in flips:
+            if all(np.array_equal(g[k][b], alt[b][0][k]) for k in keys):
+                as_flip += 1
+            else:
+                mismatched.append(b)
+    table0, lens0, table, lens, freed, nfreed = kv
+    t2, l2, f2, n2 = blocktable.kv_blocktable_truncate(table0, lens0, g["num_drop"], 16, 1)
+    kv_ok = bool(np.array_equal(table, t2) and np.array_equal(lens, l2) and
+                 np.array_equal(freed, f2) and np.array_equal(nfreed, n2))
+    return dict(step=0, sequences=len(res), exact=exact, near_tie_as_oracle=as_oracle,
+                near_tie_as_flipped=as_flip, near_tie_unresolved=unresolved,
+                mismatched=sorted(mismatched)[:16], n_mismatched=len(mismatched),
+                kv_state_equal=kv_ok)
 
 
 # --- HBM traffic from rocprofv3 counters -------------------------------------
@@ -211,6 +298,16 @@ def _traffic(launch_bytes):
         return int(t["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _dist_us(ms):
+    """Distribution of per-step times (ms in, us out): the first and last five
+    steps in order, then median, p10 and p90 over all steps."""
+    us = [round(x * 1e3, 1) for x in ms]
+    srt = sorted(us)
+    n = len(srt)
+    return dict(first5=us[:5], last5=us[-5:], median=srt[n // 2], p10=srt[n // 10],
+                p90=srt[min(n - 1, (9 * n) // 10)])
 
 
 def _draw_and_sequential_bytes(out, w, B, k, V):
@@ -423,12 +520,16 @@ def bench_tentative(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--cpu-sample", type=int, default=64, help="sequences in the oracle sample")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="minimum wall time of the oracle baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-p1-seqs", type=int, default=64,
+                    help="sequences the one-process oracle timing covers")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU baseline and parity of the timed outputs)")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="hier paths: run the step back to back this long before the counted "
+                         "warm-up steps, so that the timed steps see the clocks of sustained "
+                         "load (0: none)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="hier and tentative paths: copies of the logits the steps cycle through (1: every "
                          "step reads the same buffers, whose re-read rows the next step can "
@@ -470,20 +571,53 @@ def main():
         bench_single(args)
         return
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        procs = max(1, min(16, os.cpu_count() or 1))
-        cpu = cpu_baseline(args.cpu_sample, procs, args.cpu_seconds)
-        print(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {procs} processes",
-              file=sys.stderr, flush=True)
+    bench_hier(args)
 
+
+def _settle(step, ms, sync):
+    """Runs ``step`` back to back for ``ms`` of wall time (then synchronises):
+    the chip's power management needs tens of milliseconds of sustained load
+    before its clocks settle; a serving loop that verifies continuously runs
+    in that settled state.  Returns the number of steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(2000000 + n)
+            n += 1
+        sync()
+    return n
+
+
+def bench_hier(args):
+    """The headline: spec_verify_hier_rollback on the hierarchical workload
+    (or its lazy / by-product variants)."""
+    lazy = args.path == "hier_lazy"
+    byp = args.byproducts != "none"
+    if lazy and byp:
+        raise SystemExit("by-products need every row streamed: use --path hier")
+    headline = not lazy and not byp
     import torch
-    import lossless_token_verification_amd as sv
     import workloads
+
+    # inputs: drawn on the host for the headline (the oracle leg reads the same
+    # arrays in forked workers), on the device for the other modes
+    pool, procs = None, 0
+    if headline:
+        host = workloads.make("hier", 0, device="cpu")
+        if not args.no_cpu_baseline:
+            procs = max(1, min(HOST_SHARE, os.cpu_count() or 1))
+            pool = oracle_pool(host, procs)
+        print("[bench] host inputs ready", file=sys.stderr, flush=True)
+
+    import lossless_token_verification_amd as sv
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.make("hier", 0, device=dev)
+    if headline:
+        w = {kk: (v.to(dev) if torch.is_tensor(v) else v) for kk, v in host.items()}
+    else:
+        w = workloads.make("hier", 0, device=dev)
     B, k, V = w["B"], w["k"], w["V"]
     table0, lens0 = w["block_table"].clone(), w["seq_lens"].clone()
     ws = sv.alloc_workspace(sv.workspace_bytes(B, k, V, torch.bfloat16, 3), dev)
@@ -492,14 +626,7 @@ def main():
     print(f"[bench] workload ready: {rows} rows, {launch_bytes} B per step", file=sys.stderr,
           flush=True)
 
-    ev = HipEvents(2 * args.steps + 2)
-
-    bufs = {}
-
-    lazy = args.path == "hier_lazy"
     call = sv.spec_verify_hier_rollback_lazy if lazy else sv.spec_verify_hier_rollback
-    if lazy and args.byproducts != "none":
-        raise SystemExit("by-products need every row streamed: use --path hier")
     extra = dict(entropy=args.byproducts in ("entropy", "all"),
                  outcome=args.byproducts in ("outcome", "all"))
     extra["top_m"] = 8 if extra["outcome"] else 0
@@ -510,47 +637,69 @@ def main():
     copies = [(w["ld_logits"], w["li_logits"], w["lf_logits"])]
     for _ in range(max(1, args.rotate) - 1):
         copies.append(tuple(t.clone() for t in copies[0]))
+    # each timed step has its own outputs and its own copy of the initial KV
+    # state, so that the first timed step can be checked afterwards
+    outs = [sv.spec_verify_hier_rollback(*copies[0], w["draft_tokens"], w["temperature"],
+                                         table0.clone(), lens0.clone(),
+                                         block_size=w["block_size"], max_freed=1,
+                                         window=w["window"], seed=0, offset=999999,
+                                         workspace=ws)
+            for _ in range(args.steps)]
+    kvs = [(table0.clone(), lens0.clone()) for _ in range(args.steps)]
+    scratch_kv = (table0.clone(), lens0.clone())
     torch.cuda.synchronize()
 
-    def step(i, events=None):
+    def step(i, events=None, out=None, kv=None):
         # verification of both stages and the paged-KV rollback, one call
         ld, li, lf = copies[i % len(copies)]
-        return call(ld, li, lf,
-                    w["draft_tokens"], w["temperature"], table, lens,
-                    block_size=w["block_size"], max_freed=1,
-                    window=w["window"], seed=0, offset=i,
-                    workspace=ws, events=events, out=bufs.get("out"), **extra)
+        t, l = kv if kv is not None else scratch_kv
+        return call(ld, li, lf, w["draft_tokens"], w["temperature"], t, l,
+                    block_size=w["block_size"], max_freed=1, window=w["window"], seed=0,
+                    offset=i, workspace=ws, events=events, out=out if out is not None else outs[-1],
+                    **extra)
 
-    table, lens = table0.clone(), lens0.clone()
-    bufs["out"] = step(999999)
+    def reset_scratch_kv():
+        scratch_kv[0].copy_(table0)
+        scratch_kv[1].copy_(lens0)
+
+    settle_steps = 0
+    if args.settle_ms > 0:
+        def sync():
+            torch.cuda.synchronize()
+            reset_scratch_kv()     # the rollbacks of the settle steps must not run dry
+        settle_steps = _settle(step, args.settle_ms, sync)
     for i in range(args.warmup):
         step(1000000 + i)
     torch.cuda.synchronize()
-    table.copy_(table0)
-    lens.copy_(lens0)
-    torch.cuda.synchronize()
+    ev = HipEvents(2 * args.steps + 2)
     hip = ev.hip
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     hip.hipEventRecord(ev.ev[-2], stream)
     t_host = time.perf_counter()
     for i in range(args.steps):
-        step(i, events=(ev.ev[2 * i].value, ev.ev[2 * i + 1].value))
+        step(i, events=(ev.ev[2 * i].value, ev.ev[2 * i + 1].value), out=outs[i], kv=kvs[i])
     t_host = time.perf_counter() - t_host
     hip.hipEventRecord(ev.ev[-1], stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(2 * args.steps, 2 * args.steps + 1)
     k1_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]
+    # step i runs from its statistics kernel's start to the next step's (the
+    # last one to the closing event)
+    step_ms = [ev.elapsed_ms(2 * i, 2 * (i + 1)) for i in range(args.steps - 1)]
+    step_ms.append(ev.elapsed_ms(2 * (args.steps - 1), 2 * args.steps + 1))
     ev.close()
     if args.calibration_copy:
         calibration_copy(dev)
 
     ms_step = total_ms / args.steps
     k1_avg = sum(k1_ms) / len(k1_ms)
+    timing = {"step_us": _dist_us(step_ms), "stream_us": _dist_us(k1_ms),
+              "settle_ms": args.settle_ms, "settle_steps": settle_steps}
     if lazy:
         # bytes actually read: the L_d / L_i rows of the first N_i positions;
         # L_f rows 0..a1 of a sequence that rejects a draft there; the rest of
         # the L_d / L_i rows and every L_f row of one that accepts all N_i
-        a1 = bufs["out"]["accept_len_inter"].cpu()
+        a1 = outs[0]["accept_len_inter"].cpu()
         r0 = min(max(w["window"], 1), k)
         r1 = r0 + (1 if r0 == k else 0)
         open_ = (a1 >= r0) if r0 < k else torch.zeros_like(a1, dtype=torch.bool)
@@ -572,11 +721,11 @@ def main():
             "ld_li_rows_read": di_rows, "lf_rows_read": lf_rows,
             "hbm_gbps_read": round(read_bytes / (ms_step / 1e3) / 1e9, 1),
             "stats_phase_us": round(k1_avg * 1e3, 2),
-            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
+            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1), **timing,
         }
         print(json.dumps(line), flush=True)
         return
-    if args.byproducts != "none":
+    if byp:
         k1_gbps = launch_bytes / (k1_avg / 1e3) / 1e9
         name = {"entropy": "row entropies", "outcome": "outcome export (top 8)",
                 "all": "row entropies and outcome export (top 8)"}[args.byproducts]
@@ -596,15 +745,28 @@ def main():
                          "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                          "bytes_per_launch": launch_bytes,
                          "avg_launch_us": round(k1_avg * 1e3, 2)},
-            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
+            "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1), **timing,
         }
         print(json.dumps(line), flush=True)
         return
+
     value = B * k / (ms_step / 1e3)
     step_gbps = launch_bytes / (ms_step / 1e3) / 1e9
     k1_gbps = launch_bytes / (k1_avg / 1e3) / 1e9
     traffic = _traffic(launch_bytes)
-    reread, seq_bound = _draw_and_sequential_bytes(bufs["out"], w, B, k, V)
+    reread, seq_bound = _draw_and_sequential_bytes(outs[-1], w, B, k, V)
+    cpu, parity = None, None
+    if pool is not None:
+        print("[bench] oracle leg", file=sys.stderr, flush=True)
+        res, cpu = oracle_leg(pool, procs, B, k, 0, min(B, args.cpu_p1_seqs))
+        kv = (table0.cpu().numpy(), lens0.cpu().numpy(), kvs[0][0].cpu().numpy(),
+              kvs[0][1].cpu().numpy(), outs[0]["freed_blocks"].cpu().numpy(),
+              outs[0]["num_freed"].cpu().numpy())
+        parity = parity_of_step(pool, res, outs[0], 0, kv)
+        pool.close()
+        pool.join()
+        print(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {procs} processes, "
+              f"{cpu['p1_value']:.1f} on one; parity {parity}", file=sys.stderr, flush=True)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -625,17 +787,20 @@ def main():
         "host_enqueue_us_per_step": round(t_host / args.steps * 1e6, 1),
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_of_peak_step": round(step_gbps / HBM_PEAK_GBPS, 4),
+        **timing,
         "draw_reread_bytes_last_step": reread,
         "sequential_lower_bound_bytes_last_step": seq_bound,
+        "parity": parity,
         "roofline": {"bound": "hbm", "kernel": "rowstats_kernel<bf16>",
                      "achieved": round(k1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(k1_avg * 1e3, 2)},
-        "cpu_baseline": ({kk: v for kk, v in cpu.items() if kk != "seconds"} if cpu else None),
+        "cpu_baseline": cpu,
     }
-    if cpu:
-        line["cpu_baseline"]["value"] = round(cpu["value"], 2)
     print(json.dumps(line), flush=True)
+    if parity is not None and (parity["n_mismatched"] or not parity["kv_state_equal"]):
+        print("[bench] the first timed step differs from the oracle", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
