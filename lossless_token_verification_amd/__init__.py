@@ -25,7 +25,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# SPEC_VERIFY_LIB names another build of the same library (the host-sanitizer
+# build of the tests); by default the one built next to this file.
+LIB_PATH = os.environ.get("SPEC_VERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SV_OK = 0
 SV_ERR_INVALID_ARG = 1
