@@ -97,7 +97,15 @@ def library():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
                            "(python -c 'import __graft_entry__ as g; g.build()')")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path):
+    """A ctypes handle of a build of the library at ``path`` with the entry
+    points' signatures set (the bindings use ``library()``; a test that
+    compares two builds swaps ``_lib``)."""
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, u32, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
     lib.spec_verify_abi_version.restype = i32
@@ -141,7 +149,6 @@ def library():
     lib.spec_verify_tentative_flush.restype = i32
     lib.spec_verify_tentative_flush.argtypes = [ctypes.POINTER(Desc), P, P, i32,
                                                 ctypes.POINTER(Pending), P, P, P, P, P, sz, P]
-    _lib = lib
     return lib
 
 

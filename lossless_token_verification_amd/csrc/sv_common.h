@@ -10,7 +10,14 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;          // threads per workgroup of every kernel
+// Threads per workgroup of every kernel but the LM-head GEMM: 256, or 128 in
+// the variant build that checks the kernels for races that depend on the
+// workgroup size (libspecverify_t128.so; results must not change).
+#ifndef SV_THREADS
+#define SV_THREADS 256
+#endif
+constexpr int kThreads = SV_THREADS;
+static_assert(kThreads == 256 || kThreads == 128, "workgroup size");
 constexpr int kWave = 64;              // CDNA wavefront width
 constexpr int kWaves = kThreads / kWave;
 constexpr int kVecPerThread = 16;      // 16-byte vectors each row-stats thread holds

@@ -891,10 +891,11 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
 
   __device__ __forceinline__ void nan_draw(DrawResult& r) { r.R = r.t = r.c_lo = r.c_hi = NAN; }
 
-  // Loads the drafted tokens of sequence b into sm.toks[0, n) (threads 192..).
+  // Loads the drafted tokens of sequence b into sm.toks[0, n) (the last
+  // wavefront; n <= 63).
   template <int DT>
   __device__ __forceinline__ void load_drafts(SeqCtx<DT>& cx, int n) {
-    const int t = static_cast<int>(threadIdx.x) - 3 * kWave;
+    const int t = static_cast<int>(threadIdx.x) - (kWaves - 1) * kWave;
     if (t >= 0 && t < n) cx.sm.toks[t] = cx.a.tokens[static_cast<int64_t>(cx.b) * cx.k + t];
   }
 
@@ -975,9 +976,9 @@ __device__ __forceinline__ void unpack_vec(const u32x4& v, float (&x)[RowT<DT>::
     const int tid = threadIdx.x, k = a.k;
     const int diag_pos = k + 1;
     load_drafts(cx, k);
-    if (first && !a.hier && tid >= 2 * kWave && tid < 2 * kWave + diag_pos) {
+    if (first && !a.hier && tid >= (kWaves - 2) * kWave && tid < (kWaves - 2) * kWave + diag_pos) {
       // the single stage has no second stage: its diagnostics are empty
-      const int j = tid - 2 * kWave;
+      const int j = tid - (kWaves - 2) * kWave;
       if (a.diag_probs) {
         double* d = a.diag_probs + ((static_cast<int64_t>(b) * 2 + 1) * diag_pos + j) * 2;
         d[0] = d[1] = NAN;
