@@ -4,7 +4,7 @@
 // once, in 64 KiB chunks.  Each of the 256 threads of a workgroup issues its 16
 // nontemporal 128-bit loads up front, keeps the chunk in registers and reduces
 // it to partial softmax statistics:
-//   temperature > 0: c = round(max * s) and S = sum 2^(l * s - c), with
+//   temperature > 0: c = max * s (fp32 product) and S = sum 2^(l * s - c), with
 //                    s = log2(e) / temperature (fp32 exponent; fp32 pairwise sums,
 //                    fp64 across vectors or, for plain bf16 rows, across threads);
 //   temperature = 0: the maximum and its lowest index (greedy decoding).
