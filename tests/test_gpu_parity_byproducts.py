@@ -297,6 +297,67 @@ def test_tied_and_clustered_residuals(sv):
     assert list(tok[2, 0, 1][:4]) == [4001, 4003, 4002, 4000]
 
 
+def _exact_lists(out, w, top_m, positions):
+    """The exported lists at (b, s, j) equal the oracle's exactly: tokens in
+    order (ties in token order) and masses within PROB_ABS."""
+    tok = out["residual_tokens"].cpu().numpy()
+    mass = out["residual_mass"].cpu().numpy()
+    for b, s, j in positions:
+        p, q = _pair_rows(w, b, s, j, 1.0)
+        ref_tok, ref_mass = ob.residual_top(p, q, top_m)
+        assert list(tok[b, s, j]) == list(ref_tok), (b, s, j, tok[b, s, j], ref_tok)
+        assert np.all(np.abs(mass[b, s, j] - ref_mass) <= PROB_ABS), (b, s, j)
+
+
+def test_outcome_large_residuals_in_one_thread(sv):
+    """The largest residuals of a chunk all in groups of one thread (tokens
+    2048 apart: one lane of the kernel for 256 or 128 threads), more than its
+    list keeps: the chunk is scanned again exactly.  A second row has them in
+    two threads, a third in consecutive vectors of one thread."""
+    B, k, V = 3, 1, 70001
+    g = torch.Generator().manual_seed(93)
+    d = (torch.randn((B, k, V), generator=g) * 0.5).to(torch.bfloat16)
+    t = d[:, :1].float().repeat(1, k + 1, 1).to(torch.bfloat16)
+    for i in range(12):                       # 12 spikes, lane 5, distinct values
+        t[0, 0, 5 * 8 + i * 2048 + (i % 8)] = 6.0 + 0.25 * i
+    for i in range(12):                       # lanes 7 and 9 of chunk 1
+        t[1, 0, 32768 + (7 if i % 2 else 9) * 8 + (i // 2) * 2048 + 3] = 7.0 - 0.125 * i
+    for i in range(10):                       # vectors 16 apart (pairs of vectors)
+        t[2, 0, 12 * 8 + i * 256 * 8 * 2 + 1] = 5.0 + 0.0625 * i
+    w = {"draft_logits": d, "target_logits": t,
+         "draft_tokens": torch.zeros((B, k), dtype=torch.int32), "temperature": None}
+    out = _run(sv, w, outcome=True, top_m=8)
+    torch.cuda.synchronize()
+    check_outcome(out, w, 8)
+    _exact_lists(out, w, 8, [(0, 0, 0), (1, 0, 0), (2, 0, 0)])
+
+
+def test_outcome_ties_at_the_floor(sv):
+    """Equal residuals (equal bf16 logit pairs) around the 8th place of a
+    chunk: the tied groups are read again, and the list comes out in token
+    order.  Row 0: 30 tied tokens over the 4 chunks; row 1: 40 tied tokens in
+    one chunk, more groups than are read again (the exact rescan)."""
+    B, k, V = 2, 1, 128256
+    g = torch.Generator().manual_seed(94)
+    d = (torch.randn((B, k, V), generator=g) * 0.5).to(torch.bfloat16)
+    t = d[:, :1].float().repeat(1, k + 1, 1).to(torch.bfloat16)
+    d2 = d.clone()
+    tied0 = torch.randperm(V, generator=g)[:30]
+    tied1 = torch.randperm(32768, generator=g)[:40] + 65536
+    for b, tied in ((0, tied0), (1, tied1)):
+        t[b, 0, tied] = 4.0
+        d2[b, 0, tied] = -3.0
+    w = {"draft_logits": d2, "target_logits": t,
+         "draft_tokens": torch.zeros((B, k), dtype=torch.int32), "temperature": None}
+    out = _run(sv, w, outcome=True, top_m=8)
+    torch.cuda.synchronize()
+    check_outcome(out, w, 8)
+    _exact_lists(out, w, 8, [(0, 0, 0), (1, 0, 0)])
+    tok = out["residual_tokens"].cpu().numpy()
+    assert list(tok[0, 0, 0]) == sorted(tied0.tolist())[:8]
+    assert list(tok[1, 0, 0]) == sorted(tied1.tolist())[:8]
+
+
 def _mask(x, gen, frac, narrow_rows):
     """Masked vocabulary: a fraction `frac` of every row's logits set to -inf,
     and in `narrow_rows` (row indices of the flattened [B * n] rows) all but
