@@ -558,6 +558,10 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, Pro&& 
     B1 += static_cast<double>(b1);
     b0 = b1 = 0.0f;
   };
+  // only the rows of the stages present are read (an absent row's values
+  // are never used)
+  auto has_row = [](int e) { return e == 1 || (e == 0 ? HAS0 : HAS1); };
+  auto elem_at = [&](int e, int v) { return has_row(e) ? load_elem(base[e], v, DT) : 0.0f; };
   const bool vec = ((reinterpret_cast<uintptr_t>(base[0]) | reinterpret_cast<uintptr_t>(base[1]) |
                      reinterpret_cast<uintptr_t>(base[2])) & 15) == 0;
   if (vec) {
@@ -574,7 +578,8 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, Pro&& 
       for (int q = 0; q < kBatch; ++q) {
         const int vc = min((i0 + q) * kThreads + tid, nfull - 1);
 #pragma unroll
-        for (int e = 0; e < 3; ++e) w[e][q] = __builtin_nontemporal_load(vr[e] + vc);
+        for (int e = 0; e < 3; ++e)
+          if (has_row(e)) w[e][q] = __builtin_nontemporal_load(vr[e] + vc);
       }
     };
     // a pair of vectors (tokens v0.. and v0 + kThreads * VPE..) is one group
@@ -588,7 +593,8 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, Pro&& 
         if (vi >= nfull) continue;
         float x[3][VPE];
 #pragma unroll
-        for (int e = 0; e < 3; ++e) unpack_vec<DT, VPE>(w[e][q], x[e]);
+        for (int e = 0; e < 3; ++e)
+          if (has_row(e)) unpack_vec<DT, VPE>(w[e][q], x[e]);
 #pragma unroll
         for (int g = 0; g < VPE; ++g) {
           pair_elem<HAS0, HAS1>(k, x[0][g], x[1][g], x[2][g], r0[q][g], r1[q][g]);
@@ -617,12 +623,12 @@ __device__ inline void pair_scan(const char* const* base, int e0, int e1, Pro&& 
       }
     }
     const int v = e0 + nfull * VPE + tid;
-    if (v < e1) visit(load_elem(base[0], v, DT), load_elem(base[1], v, DT), load_elem(base[2], v, DT), v);
+    if (v < e1) visit(elem_at(0, v), elem_at(1, v), elem_at(2, v), v);
   } else {
     k = pro();
     int n = 0;
     for (int v = e0 + tid; v < e1; v += kThreads) {
-      visit(load_elem(base[0], v, DT), load_elem(base[1], v, DT), load_elem(base[2], v, DT), v);
+      visit(elem_at(0, v), elem_at(1, v), elem_at(2, v), v);
       if (++n == 8) {
         flush();
         n = 0;
@@ -758,11 +764,15 @@ __global__ __launch_bounds__(kThreads) void pair_kernel(ByArgs a) {
     for (int q = 0; q < 2; ++q) {
       const int vb = v0 + q * kStride;
       if (vb >= vend) break;
+      // the stage's two rows (the other one's values are left unused)
       float x[3][VPE];
 #pragma unroll
-      for (int e = 0; e < 3; ++e)
-        unpack_vec<DT, VPE>(*reinterpret_cast<const u32x4*>(base[e] + static_cast<int64_t>(vb) * ES),
-                            x[e]);
+      for (int e = 0; e < 3; ++e) {
+        const bool need = e == 1 || e == (st == 0 ? 0 : 2);
+        const u32x4 raw = need ? *reinterpret_cast<const u32x4*>(base[e] + static_cast<int64_t>(vb) * ES)
+                               : u32x4{0u, 0u, 0u, 0u};
+        unpack_vec<DT, VPE>(raw, x[e]);
+      }
 #pragma unroll
       for (int g = 0; g < VPE; ++g) {
         float r0, r1;
