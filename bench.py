@@ -10,7 +10,7 @@ timed region.
 
 Before the counted warm-up steps the step runs back to back for --settle-ms
 (400 ms by default): in the first tens of milliseconds of sustained load the
-chip's power management holds the shader clock at 1.5-1.9 GHz before it
+chip's power management holds the shader clock at 1.2-1.9 GHz before it
 settles at 2.2-2.3 GHz, and a serving loop that verifies continuously runs in
 the settled state.  The timed steps are full steps; the line reports each
 step's time distribution beside the total.
