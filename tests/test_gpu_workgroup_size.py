@@ -114,6 +114,33 @@ def test_rollback_call_at_128_threads(both):
     assert torch.equal(ta[same], tb[same]) and torch.equal(la[same], lb[same])
 
 
+BYP = [("hier", 6, 8, 70001, "bf16", (1.0,), 8), ("hier", 5, 4, 20011, "f32", (0.0, 0.7, 1.0), 3),
+       ("single", 6, 4, 3001, "bf16", (1.0, 0.5), 8)]
+
+
+@pytest.mark.parametrize("case", BYP, ids=lambda c: f"{c[0]}B{c[1]}k{c[2]}V{c[3]}{c[4]}m{c[6]}")
+def test_byproducts_at_128_threads(both, case):
+    """Row entropies and the outcome export (the lane sets, candidate buffers
+    and per-stage thread halves of the outcome pass scale with the workgroup)
+    on both builds, each against the oracle."""
+    from tests import test_gpu_parity_byproducts as tb
+    sv, lib256, lib128 = both
+    kind, B, k, V, dt, temps, top_m = case
+    if kind == "hier":
+        w = workloads.make_hier(B, k, V, dtype=dt, temps=temps, window=4, seed=(144, B, V),
+                                ctx=(16, 64))
+    else:
+        w = workloads.make_single(B, k, V, dtype=dt, temps=temps, seed=(145, B, V))
+    outs = [_on(sv, lib, lambda: tb._run(sv, w, 3, 4, entropy=True, outcome=True, top_m=top_m))
+            for lib in (lib256, lib128)]
+    for out in outs:
+        tb.check_entropy(out["entropy"].cpu().numpy(), w)
+        assert tb.check_outcome(out, w, top_m) > 0
+    a, b = (o["accept_mass"].cpu().numpy() for o in outs)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.nanmax(np.abs(a - b)) <= 1e-6
+
+
 def _agree(a, b, ref, keys, B):
     """The two builds give the same outputs on every sequence without a near
     tie (at a near tie either may take the other outcome)."""
