@@ -452,7 +452,7 @@ int32_t make_lm_plan(const spec_verify_desc* d, int32_t hidden, LmPlan* p) {
     return fail(SV_ERR_UNSUPPORTED, "vocab > " + std::to_string(SV_MAX_VOCAB));
   if (d->dtype != SV_DTYPE_BF16)
     return fail(SV_ERR_UNSUPPORTED, "the LM-head path takes bf16 hidden states and head");
-  if (hidden < sv::kGemmKT || hidden % sv::kGemmKT != 0 || hidden > SV_MAX_HIDDEN)
+  if (hidden < sv::kHiddenMultiple || hidden % sv::kHiddenMultiple != 0 || hidden > SV_MAX_HIDDEN)
     return fail(SV_ERR_UNSUPPORTED, "hidden must be a multiple of 64 in [64, " +
                                         std::to_string(SV_MAX_HIDDEN) + "]");
   const int64_t ldw = d->row_stride == 0 ? hidden : d->row_stride;
@@ -559,7 +559,7 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
   if (err != hipSuccess) return device_error(err, "LM-head statistics launch");
 
   sv::MergeArgs ma{part, merged, g.M, p.n_tiles, seqw, 2 * B, flags};
-  err = sv::launch_merge(ma, st);
+  err = sv::launch_merge(ma, g, st);
   if (err != hipSuccess) return device_error(err, "merge launch");
 
   sv::VerifyArgs va{};

@@ -79,13 +79,6 @@ __global__ __launch_bounds__(kThreads) void entropy_kernel(ByArgs a) {
   a.entropy[row] = static_cast<float>(H);
 }
 
-// Residuals and probabilities here are non-negative floats (or +0), whose
-// bit patterns order like unsigned integers: min and max run as integer
-// operations, exact and free of the float min NaN handling.
-__device__ __forceinline__ float uminf(float a, float b) {
-  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
-}
-
 // Per-thread lists of the largest residuals, largest first; elements arrive
 // in increasing token order, so strict comparisons keep equal values in token
 // order.
@@ -213,7 +206,6 @@ static_assert(kWave % kGroupLanes == 0, "a lane group lies within one wavefront"
 struct PairShared {
   float key[kWaves];
   int32_t idx[kWaves];
-  double sum[kWaves];
   float c[3];     // per row: the merged reference c
   double S[3];    // per row: the merged S
   double S1[3];   // per row: the merged S relative to c' (pair_kernel)
@@ -233,18 +225,6 @@ struct PairShared {
   uint2 cand[2][kWaves][kCandCap];   // (residual bits, key)
   uint2 sel[2][kMaxExpand * kGroupElems];   // their elements >= floor: (residual bits, token)
 };
-
-__device__ inline float block_max(float v, PairShared& sh) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  v = wave_max(v);
-  if (lane == 0) sh.key[wave] = v;
-  __syncthreads();
-  float m = sh.key[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, sh.key[w]);
-  __syncthreads();
-  return m;
-}
 
 // Workgroup top-m of the threads' TopLists: m rounds of a (value, token)
 // arg-max; the winning thread drops its head.  Thread 0 writes the chunk's
@@ -475,18 +455,6 @@ __device__ inline bool pair_lists(bool has0, bool has1, const Top3& L0, const To
       out->tok[q] = -1;
     }
   return true;
-}
-
-__device__ inline double block_sum(double v, PairShared& sh) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  v = wave_sum(v);
-  if (lane == 0) sh.sum[wave] = v;
-  __syncthreads();
-  double s = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += sh.sum[w];
-  __syncthreads();
-  return s;
 }
 
 // Constants of one workgroup's rows (see pair_kernel): s = log2(e) / tau, the

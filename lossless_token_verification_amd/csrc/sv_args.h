@@ -112,10 +112,10 @@ struct KvArgs {
 // r - m_draft (a_target); with `a_rows`, GEMM row r takes A row a_rows[r]
 // (-1: the row is skipped).  Epilogues:
 //  - stats: partial softmax statistics of every (row, N tile), in the Partial
-//    format of the row-statistics kernel, and the logit at the row's drafted
-//    token (draft row b*k + j and target row b*(k+1) + j, j < k, hold token
-//    tokens[b*k + j]);
+//    format of the row-statistics kernel;
 //  - rows: the fp32 logits themselves, out[r * ldo + v].
+// Draft row b*k + j and target row b*(k+1) + j, j < k, hold drafted token
+// tokens[b*k + j]; the merge forms the logit there into gath[r].
 struct GemmArgs {
   const uint16_t* a_draft;
   const uint16_t* a_target;
@@ -131,9 +131,10 @@ struct GemmArgs {
   float* out;               // [M, ldo]
   int64_t ldo;
 };
-// Merges the n partials of each of `rows` rows into one (nc = 1 format).
-// The first workgroups also zero `clear_words` and the flag word (the
-// counters of the verification launches that follow).
+// Merges the n partials of each of `rows` rows into one (nc = 1 format) and
+// writes each row's drafted-token logit (GemmArgs.gath).  The first
+// workgroups also zero `clear_words` and the flag word (the counters of the
+// verification launches that follow).
 struct MergeArgs {
   const Partial* in;
   Partial* out;
@@ -148,11 +149,13 @@ constexpr int kGemmNT = 256;   // vocabulary entries per GEMM workgroup tile
 constexpr int kGemmWM = 2;     // wavefronts of a GEMM workgroup along rows
 constexpr int kGemmWN = 4;     // and along the vocabulary
 constexpr int kGemmKT = 64;    // hidden elements per pipeline step
+constexpr int kHiddenMultiple = 64;   // the LM-head call's hidden size is a multiple of this
+static_assert(kHiddenMultiple % kGemmKT == 0, "whole pipeline steps");
 
 hipError_t launch_lmhead_stats(const GemmArgs& a, hipStream_t st, hipEvent_t ev_start = nullptr,
                                hipEvent_t ev_stop = nullptr);
 hipError_t launch_lmhead_rows(const GemmArgs& a, hipStream_t st);
-hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, const GemmArgs& g, hipStream_t st);
 
 // By-products of a verification call: the entropy of every streamed row
 // (from the chunk partials and their T), and per tested position the
