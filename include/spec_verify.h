@@ -329,9 +329,10 @@ size_t spec_verify_lmhead_workspace_bytes(const spec_verify_desc* desc, int32_t 
  * h_draft[b, j] . W^T and p the softmax of h_target[b, j] . W^T.  The rule is
  * then exactly spec_verify_single's.  The logits are formed on the matrix
  * cores (bf16 products, fp32 sums) and never stored: the softmax statistics
- * and the logits at the drafted tokens are reduced from each output tile, and
- * after the decisions only the rows each sequence draws from (p at the stop
- * position and, for a correction, q there) are recomputed.
+ * are reduced from each output tile, the logits at the drafted tokens are
+ * formed as dot products (fp32 sums), and after the decisions only the rows
+ * each sequence draws from (p at the stop position and, for a correction, q
+ * there) are recomputed.
  *   desc           dtype must be SV_DTYPE_BF16; vocab = V; row_stride = the
  *                  head's row stride in elements (0 => hidden), a multiple
  *                  of 8
