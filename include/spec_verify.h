@@ -345,7 +345,7 @@ size_t spec_verify_lmhead_workspace_bytes(const spec_verify_desc* desc, int32_t 
  *   the three must be 16-byte aligned; other arguments as for
  *   spec_verify_single (diag.stats_begin/end bracket the statistics GEMM)
  *   workspace      >= spec_verify_lmhead_workspace_bytes(desc, hidden): about
- *                  B*(2k+1)*ceil(V/256)*16 bytes of tile statistics plus
+ *                  B*(2k+1)*ceil(V/384)*16 bytes of tile statistics plus
  *                  2*B*V*4 bytes of recomputed rows
  * Errors as for spec_verify_single; a bf16 requirement or hidden size outside
  * the limits is SV_ERR_UNSUPPORTED.

@@ -602,6 +602,7 @@ int32_t run_lmhead(const spec_verify_desc* desc, int32_t hidden, const void* h_d
 
   sv::GemmArgs r = g;
   r.a_rows = stop_rows;
+  r.n_tiles = (desc->vocab + sv::kGemmRowsNT - 1) / sv::kGemmRowsNT;
   r.M = 2 * B;
   r.out = rows;
   r.ldo = p.ldo;

@@ -1,7 +1,7 @@
 // LM-head path: the logits of the draft and final exits are never written to
 // memory.  A bf16 GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16) multiplies
 // the exits' hidden states by the shared head W [V, d] and reduces each
-// 192 x 256 output tile in its epilogue to the per-(row, vocabulary tile)
+// 192 x 384 output tile in its epilogue to the per-(row, vocabulary tile)
 // softmax partials; a merge launch combines them per row and forms the logit
 // at each row's drafted token (one dot product per row).  After the
 // decisions, the same GEMM recomputes only the two rows each sequence draws
@@ -12,7 +12,8 @@
 // distribution (HiSpec summary, section 2 "Kernmechanismus"); with a linear
 // head the distribution is the softmax of hidden . W^T.
 //
-// Tiling (512 threads, 2 x 4 wavefronts of 96 x 64 outputs each): both
+// Tiling (512 threads, 2 x 4 wavefronts of 96 x 96 outputs each; the
+// recompute GEMM 256 x 256 tiles, 128 x 64 per wavefront): both
 // operands are K-contiguous (hidden states [rows, d], head [V, d]), so each
 // 64-element K step of the A and W tiles is loaded from global memory straight
 // into LDS (16-byte direct loads, no register stage, rows of 128 bytes with an
@@ -79,7 +80,7 @@ __device__ __forceinline__ int swz(int r, int kv) {
 
 // statistics over all B(2k+1) rows; recompute of the 2B stopped rows
 using StatsCfg = GemmCfg<kGemmMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
-using RowsCfg = GemmCfg<kGemmRowsMT, kGemmNT, kGemmWM, kGemmWN, kGemmKT>;
+using RowsCfg = GemmCfg<kGemmRowsMT, kGemmRowsNT, kGemmWM, kGemmWN, kGemmKT>;
 
 // Sums over each 32-lane half of a wavefront (the lanes holding one output
 // row of a 32 x 32 MFMA tile) with DPP moves on the VALU: a scan within each

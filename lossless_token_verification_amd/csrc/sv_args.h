@@ -145,7 +145,8 @@ struct MergeArgs {
 };
 constexpr int kGemmMT = 192;   // rows per GEMM workgroup tile (statistics GEMM)
 constexpr int kGemmRowsMT = 256;  // rows per tile of the recompute GEMM (2B rows)
-constexpr int kGemmNT = 256;   // vocabulary entries per GEMM workgroup tile
+constexpr int kGemmNT = 384;   // vocabulary entries per GEMM workgroup tile (statistics GEMM)
+constexpr int kGemmRowsNT = 256;  // and per tile of the recompute GEMM
 constexpr int kGemmWM = 2;     // wavefronts of a GEMM workgroup along rows
 constexpr int kGemmWN = 4;     // and along the vocabulary
 constexpr int kGemmKT = 64;    // hidden elements per pipeline step

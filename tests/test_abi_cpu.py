@@ -134,14 +134,15 @@ def test_verify_host_checks_without_gpu(sv):
 
 def test_lmhead_workspace_formula_and_checks(sv):
     """LM-head plan: flags + 8 B per sequence + draw-tile sums of fp32 rows +
-    one 16-byte partial per (GEMM row, 256-entry vocabulary tile) + merged
-    partials + gathered logits + stopped-row ids + two fp32 rows per sequence."""
+    one 16-byte partial per (GEMM row, 384-entry vocabulary tile of the
+    statistics GEMM) + merged partials + gathered logits + stopped-row ids +
+    two fp32 rows per sequence."""
     def pad(n):
         return (n + 255) // 256 * 256
     B, k, V, d = 128, 4, 128256, 4096
     M = B * (2 * k + 1)
     nt = -(-V // 256)
-    want = (256 + pad(B * 8) + pad(B * 2 * nt * 4) + pad(M * (-(-V // 256)) * 16) +
+    want = (256 + pad(B * 8) + pad(B * 2 * nt * 4) + pad(M * (-(-V // 384)) * 16) +
             pad(M * 16) + pad(M * 4) + pad(2 * B * 4) + 2 * B * V * 4)
     assert sv.lmhead_workspace_bytes(B, k, V, d) == want
     assert sv.lmhead_workspace_bytes(3, 2, 1001, 64) > 0
