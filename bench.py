@@ -18,7 +18,10 @@ step's time distribution beside the total.
 Prints one JSON line: verified draft tokens/s (B*k per step), whole-step and
 row-statistics-kernel HBM bandwidth against the 8 TB/s peak, the oracle timed
 on the first timed step's inputs on this host's cores, and the parity of that
-step's outputs with the oracle's.
+step's outputs with the oracle's.  After the timed steps, the other workloads
+(the single-stage ones, call by call with their parity, and the fused LM-head
+verify) are measured into the line's "other_workloads" (--no-other-workloads
+skips them).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--settle-ms 400]
 """
@@ -332,17 +335,16 @@ def _draw_and_sequential_bytes(out, w, B, k, V):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_lmhead(args):
+def measure_lmhead(steps, warmup, dev):
     """The fused LM-head verify (B=128, k=4, d=4096, V=128256, bf16 hidden
-    states and head): one spec_verify_lmhead_single call per step.  Reports
-    verified draft tokens/s and the statistics GEMM's rate against the bf16
-    dense MFMA peak (2 * rows * V * d flops per launch, rows = B * (2k + 1))."""
+    states and head): ``steps`` spec_verify_lmhead_single calls back to back,
+    each with the statistics GEMM bracketed by its own HIP events.  Returns
+    the per-call time and the statistics GEMM's rate against the bf16 dense
+    MFMA peak (2 * rows * V * d flops per launch, rows = B * (2k + 1))."""
     import torch
     import lossless_token_verification_amd as sv
     import workloads
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     w = workloads.make("lmhead", 0, device=dev)
     B, k, V, d = w["B"], w["k"], w["V"], w["d"]
     ws = sv.alloc_workspace(sv.lmhead_workspace_bytes(B, k, V, d), dev)
@@ -350,7 +352,7 @@ def bench_lmhead(args):
     flops = 2.0 * rows * V * d
     print(f"[bench] LM-head workload ready: {rows} rows, {flops / 1e12:.3f} TFLOP per GEMM",
           file=sys.stderr, flush=True)
-    ev = HipEvents(2 * args.steps + 2)
+    ev = HipEvents(2 * steps + 2)
     bufs = {}
 
     def step(i, events=None):
@@ -360,99 +362,186 @@ def bench_lmhead(args):
                                             out=bufs.get("out"))
 
     bufs["out"] = step(999999)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(1000000 + i)
     torch.cuda.synchronize()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     ev.hip.hipEventRecord(ev.ev[-2], stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, events=(ev.ev[2 * i].value, ev.ev[2 * i + 1].value))
     ev.hip.hipEventRecord(ev.ev[-1], stream)
     torch.cuda.synchronize()
-    total_ms = ev.elapsed_ms(2 * args.steps, 2 * args.steps + 1)
-    g_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]
+    total_ms = ev.elapsed_ms(2 * steps, 2 * steps + 1)
+    g_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
     ev.close()
-    ms_step = total_ms / args.steps
     g_avg = sum(g_ms) / len(g_ms)
     tflops = flops / (g_avg / 1e3) / 1e12
+    return dict(B=B, k=k, V=V, d=d, ms_per_call=round(total_ms / steps, 5),
+                roofline={"bound": "mfma", "kernel": "lmhead_gemm<stats>",
+                          "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "traffic": None, "flops_per_launch": flops,
+                          "avg_launch_us": round(g_avg * 1e3, 2)})
+
+
+def bench_lmhead(args):
+    """The fused LM-head verify as the step (see measure_lmhead)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = measure_lmhead(args.steps, args.warmup, dev)
+    B, k, V, d, ms_step = m["B"], m["k"], m["V"], m["d"], m["ms_per_call"]
     line = {
         "metric": "verified draft tokens/s, fused LM-head verify B=128 k=4 d=4096 V=128256 bf16",
         "value": round(B * k / (ms_step / 1e3), 1),
         "unit": "verified draft tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "fused LM-head single-stage verify, B=128 k=4 d=4096 "
                                "V=128256, bf16 hidden states and head", "B": B, "k": k,
                    "d": d, "V": V},
-        "roofline": {"bound": "mfma", "kernel": "lmhead_gemm<stats>",
-                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": flops,
-                     "avg_launch_us": round(g_avg * 1e3, 2)},
+        "roofline": m["roofline"],
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
 
-def bench_single(args):
+SINGLE_KEYS = ("accept_len", "out_tokens", "num_emitted", "num_drop")
+
+
+def _single_parity(w, gpu, offset):
+    """One single-stage call's GPU outputs against the oracle's on the same
+    inputs, as parity_of_step does for the headline: bit for bit where the
+    outcome is unique, the oracle's outcome or the one with that near-tie
+    decision flipped otherwise."""
+    import numpy as np
+    import workloads
+    from oracle import verify
+    d = workloads.to_numpy_raw(w["draft_logits"])
+    t = workloads.to_numpy_raw(w["target_logits"])
+    tok = w["draft_tokens"].cpu().numpy()
+    temp = w["temperature"].cpu().numpy() if w.get("temperature") is not None else None
+    ref = verify.spec_verify_single(d, t, tok, temp, 0, offset)
+    g = {k: gpu[k].cpu().numpy() for k in SINGLE_KEYS}
+    exact = as_oracle = as_flip = unresolved = 0
+    mismatched = []
+    for b in range(w["B"]):
+        same = all(np.array_equal(g[k][b], ref[k][b]) for k in SINGLE_KEYS)
+        ev = verify.near_tie_event(ref["infos"][b], 1e-5, 1e-6)
+        if ev is None:
+            exact += 1
+            if not same:
+                mismatched.append(b)
+        elif same:
+            as_oracle += 1
+        elif ev["flip"] is None:
+            unresolved += 1
+        else:
+            alt = verify.spec_verify_single(d, t, tok, temp, 0, offset, sequences=[b],
+                                            flips={b: ev})
+            if all(np.array_equal(g[k][b], alt[k][b]) for k in SINGLE_KEYS):
+                as_flip += 1
+            else:
+                mismatched.append(b)
+    return dict(sequences=w["B"], exact=exact, near_tie_as_oracle=as_oracle,
+                near_tie_as_flipped=as_flip, near_tie_unresolved=unresolved,
+                mismatched=mismatched[:16], n_mismatched=len(mismatched))
+
+
+def measure_single(name, steps, warmup, dev, parity=False):
     """The single-stage verify on one of the single-stage workloads.  Each call
     is bracketed by its own HIP events; between calls a 1 GiB buffer is
     written (outside the events), so that the logits are not served from the
     256 MB memory-side cache ("cold"); a second pass without it gives the
-    warm figure.  Algorithmic bytes: every draft and target row read once."""
+    warm figure.  Algorithmic bytes: every draft and target row read once.
+    With ``parity`` the first timed call's outputs are compared with the
+    oracle's."""
     import torch
     import lossless_token_verification_amd as sv
     import workloads
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = workloads.make(args.workload, 0, device=dev)
+    w = workloads.make(name, 0, device=dev)
     B, k, V = w["B"], w["k"], w["V"]
     es = 2 if w["dtype"] == "bf16" else 4
     algo = B * (2 * k + 1) * V * es
     ws = sv.alloc_workspace(sv.workspace_bytes(B, k, V, w["draft_logits"].dtype, 2), dev)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    ev = HipEvents(2 * args.steps)
-    out = {}
+    ev = HipEvents(2 * steps)
+    first = {}
 
     def call(i):
         return sv.spec_verify_single(w["draft_logits"], w["target_logits"], w["draft_tokens"],
                                      w.get("temperature"), seed=0, offset=i, workspace=ws)
 
-    for i in range(args.warmup):
-        call(i)
+    for i in range(warmup):
+        call(1000000 + i)
     torch.cuda.synchronize()
     res = {}
     for mode in ("cold", "warm"):
-        for i in range(args.steps):
+        for i in range(steps):
             if mode == "cold":
                 flush.fill_(float(i))
             ev.hip.hipEventRecord(ev.ev[2 * i], stream)
-            call(i)
+            out = call(i)
             ev.hip.hipEventRecord(ev.ev[2 * i + 1], stream)
+            if mode == "cold" and i == 0:
+                first = out
         torch.cuda.synchronize()
-        ts = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(args.steps))
+        ts = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(steps))
         res[mode] = dict(median_us=round(ts[len(ts) // 2], 2), p10_us=round(ts[len(ts) // 10], 2),
                          p90_us=round(ts[(9 * len(ts)) // 10], 2))
     ev.close()
+    del flush
     us = res["cold"]["median_us"]
     gbps = algo / (us * 1e-6) / 1e9
+    m = dict(workload=name, B=B, k=k, V=V, logits=w["dtype"],
+             value=round(B * k / (us * 1e-6), 1), unit="verified draft tokens/s",
+             per_call=res,
+             roofline_call={"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                            "bytes_per_call": algo,
+                            "t_roof_us": round(algo / (HBM_PEAK_GBPS * 1e9) * 1e6, 2)})
+    if parity:
+        m["parity"] = _single_parity(w, first, 0)
+    return m
+
+
+def bench_single(args):
+    """The single-stage verify on --workload as the step (see measure_single)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = measure_single(args.workload, args.steps, args.warmup, dev)
+    us = m["per_call"]["cold"]["median_us"]
     line = {
         "metric": f"verified draft tokens/s, single-stage verify, {args.workload} workload",
-        "value": round(B * k / (us * 1e-6), 1), "unit": "verified draft tokens/s",
+        "value": m["value"], "unit": "verified draft tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "k": k, "V": V, "logits": w["dtype"]},
-        "per_call": res,
-        "roofline_call": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                          "bytes_per_call": algo,
-                          "t_roof_us": round(algo / (HBM_PEAK_GBPS * 1e9) * 1e6, 2)},
+        "config": {"workload": args.workload, "B": m["B"], "k": m["k"], "V": m["V"],
+                   "logits": m["logits"]},
+        "per_call": m["per_call"],
+        "roofline_call": m["roofline_call"],
     }
     print(json.dumps(line), flush=True)
+
+
+def other_workloads(dev, parity):
+    """The workloads beside the headline, measured after its timed steps (not
+    part of the step): the three single-stage workloads (20 cold and 20 warm
+    calls each; with ``parity``, part of the oracle leg, the first cold call's
+    outputs compared with the oracle) and the fused LM-head verify (10
+    calls)."""
+    res = {}
+    for name in ("tiny", "batched", "mixed_temp"):
+        print(f"[bench] other workload: {name}", file=sys.stderr, flush=True)
+        res[name] = measure_single(name, 20, 5, dev, parity=parity)
+    print("[bench] other workload: lmhead", file=sys.stderr, flush=True)
+    res["lmhead"] = measure_lmhead(10, 3, dev)
+    return res
 
 
 def bench_tentative(args):
@@ -547,6 +636,9 @@ def main():
                          "the single-stage verify on --workload")
     ap.add_argument("--workload", choices=("tiny", "batched", "mixed_temp"), default="batched",
                     help="single path only: the single-stage workload")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="headline only: skip the single-stage and LM-head workloads measured "
+                         "after the timed steps")
     ap.add_argument("--byproducts", choices=("none", "entropy", "outcome", "all"), default="none",
                     help="hier path only: also compute the row entropies, the outcome export "
                          "(acceptance mass and the 8 largest residual tokens per position), "
@@ -767,6 +859,9 @@ def bench_hier(args):
         pool.join()
         print(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {procs} processes, "
               f"{cpu['p1_value']:.1f} on one; parity {parity}", file=sys.stderr, flush=True)
+    others = None
+    if not args.no_other_workloads:
+        others = other_workloads(dev, parity=not args.no_cpu_baseline)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -796,10 +891,15 @@ def bench_hier(args):
                      "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(k1_avg * 1e3, 2)},
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
     if parity is not None and (parity["n_mismatched"] or not parity["kv_state_equal"]):
         print("[bench] the first timed step differs from the oracle", file=sys.stderr)
+        sys.exit(1)
+    bad = [n for n, m in (others or {}).items() if m.get("parity", {}).get("n_mismatched")]
+    if bad:
+        print(f"[bench] outputs differ from the oracle on: {', '.join(bad)}", file=sys.stderr)
         sys.exit(1)
 
 
