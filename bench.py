@@ -335,7 +335,7 @@ def _draw_and_sequential_bytes(out, w, B, k, V):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def measure_lmhead(steps, warmup, dev):
+def measure_lmhead(steps, warmup, dev, settle_ms=0.0):
     """The fused LM-head verify (B=128, k=4, d=4096, V=128256, bf16 hidden
     states and head): ``steps`` spec_verify_lmhead_single calls back to back,
     each with the statistics GEMM bracketed by its own HIP events.  Returns
@@ -362,6 +362,7 @@ def measure_lmhead(steps, warmup, dev):
                                             out=bufs.get("out"))
 
     bufs["out"] = step(999999)
+    settle_steps = _settle(step, settle_ms, torch.cuda.synchronize) if settle_ms > 0 else 0
     for i in range(warmup):
         step(1000000 + i)
     torch.cuda.synchronize()
@@ -377,6 +378,7 @@ def measure_lmhead(steps, warmup, dev):
     g_avg = sum(g_ms) / len(g_ms)
     tflops = flops / (g_avg / 1e3) / 1e12
     return dict(B=B, k=k, V=V, d=d, ms_per_call=round(total_ms / steps, 5),
+                settle_ms=settle_ms, settle_steps=settle_steps,
                 roofline={"bound": "mfma", "kernel": "lmhead_gemm<stats>",
                           "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -389,7 +391,7 @@ def bench_lmhead(args):
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    m = measure_lmhead(args.steps, args.warmup, dev)
+    m = measure_lmhead(args.steps, args.warmup, dev, args.settle_ms)
     B, k, V, d, ms_step = m["B"], m["k"], m["V"], m["d"], m["ms_per_call"]
     line = {
         "metric": "verified draft tokens/s, fused LM-head verify B=128 k=4 d=4096 V=128256 bf16",
@@ -403,6 +405,7 @@ def bench_lmhead(args):
                    "d": d, "V": V},
         "roofline": m["roofline"],
         "cpu_baseline": None,
+        "settle_ms": m["settle_ms"], "settle_steps": m["settle_steps"],
     }
     print(json.dumps(line), flush=True)
 
@@ -577,6 +580,7 @@ def bench_tentative(args):
         return sv.spec_verify_tentative_flush(lf_i, w["temperature"], pend, min_pending=1,
                                               seed=0, offset=2 * i, workspace=ws)
 
+    settle_steps = _settle(step, args.settle_ms, torch.cuda.synchronize) if args.settle_ms > 0 else 0
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -602,6 +606,7 @@ def bench_tentative(args):
                                "of the pending tokens against the final exit",
                    "B": B, "k": k, "V": V, "capacity": cap, "input_copies": len(copies)},
         "approx_rows_read_per_step": rows_read,
+        "settle_ms": args.settle_ms, "settle_steps": settle_steps,
     }
     print(json.dumps(line), flush=True)
 
@@ -616,9 +621,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU baseline and parity of the timed outputs)")
     ap.add_argument("--settle-ms", type=float, default=400.0,
-                    help="hier paths: run the step back to back this long before the counted "
-                         "warm-up steps, so that the timed steps see the clocks of sustained "
-                         "load (0: none)")
+                    help="hier, lmhead and tentative paths: run the step back to back this "
+                         "long before the counted warm-up steps, so that the timed steps see "
+                         "the clocks of sustained load (0: none)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="hier and tentative paths: copies of the logits the steps cycle through (1: every "
                          "step reads the same buffers, whose re-read rows the next step can "
