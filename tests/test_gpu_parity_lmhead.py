@@ -39,6 +39,7 @@ SMALL = [
     (5, 2, 192, 129, 0.3, (1.0,)),            # one row tile, V just past a tile
     (3, 0, 64, 777, 0.3, (1.0,)),             # k = 0: bonus only
     (2, 63, 64, 300, 0.1, (1.0,)),            # k = 63
+    (1, 1, 65536, 300, 0.004, (1.0,)),        # d = SV_MAX_HIDDEN: 1024 K steps
     (9, 5, 512, 20011, 0.05, (1.3,)),         # several M tiles, flat rows
     # 2B = 280 recomputed rows: a second, partial recompute tile; 420 GEMM rows
     (140, 1, 128, 3000, 0.2, (1.0, 0.0)),
