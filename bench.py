@@ -537,13 +537,14 @@ def other_workloads(dev, parity):
     part of the step): the three single-stage workloads (20 cold and 20 warm
     calls each; with ``parity``, part of the oracle leg, the first cold call's
     outputs compared with the oracle) and the fused LM-head verify (10
-    calls)."""
+    calls after 200 ms of back-to-back calls: the oracle leg leaves the GPU
+    idle long enough for its clocks to drop)."""
     res = {}
     for name in ("tiny", "batched", "mixed_temp"):
         print(f"[bench] other workload: {name}", file=sys.stderr, flush=True)
         res[name] = measure_single(name, 20, 5, dev, parity=parity)
     print("[bench] other workload: lmhead", file=sys.stderr, flush=True)
-    res["lmhead"] = measure_lmhead(10, 3, dev)
+    res["lmhead"] = measure_lmhead(10, 3, dev, settle_ms=200.0)
     return res
 
 
