@@ -77,10 +77,12 @@ SMALL_SINGLE = [
     (5, 0, 4096, "f32", "normal", 2.0, (0.8, 0.8), (1.0,)),            # k = 0: bonus only
     (3, 63, 2048, "bf16", "normal", 1.0, (0.95, 0.99), (1.0,)),        # k = 63
     (4, 2, 1, "f32", "normal", 1.0, (0.5, 0.5), (1.0,)),               # V = 1
+    (8, 4, 30011, "f32", "normal", 3.0, (0.5, 0.95), (0.05, 0.01)),    # sharp: tau << 1
+    (8, 4, 10007, "bf16", "normal", 3.0, (0.5, 0.9), (8.0,)),          # flat: tau >> 1
 ]
 
 
-@pytest.mark.parametrize("case", SMALL_SINGLE, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}")
+@pytest.mark.parametrize("case", SMALL_SINGLE, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}t{c[7][-1]}")
 def test_single_small_parity(sv, case):
     B, k, V, dt, law, scale, alpha, temps = case
     report = {}
@@ -103,10 +105,12 @@ SMALL_HIER = [
     (6, 5, 3001, "bf16", (1.0,), 1),          # misaligned rows, window 1
     (4, 3, 9000, "f32", (0.9,), 2),
     (3, 0, 5000, "bf16", (1.0,), 4),          # k = 0
+    (6, 5, 20011, "bf16", (0.05, 0.02), 4),   # sharp distributions
+    (6, 5, 20011, "f32", (10.0,), 2),         # flat distributions, long acceptance runs
 ]
 
 
-@pytest.mark.parametrize("case", SMALL_HIER, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}w{c[5]}")
+@pytest.mark.parametrize("case", SMALL_HIER, ids=lambda c: f"B{c[0]}k{c[1]}V{c[2]}{c[3]}w{c[5]}t{c[4][-1]}")
 def test_hier_small_parity(sv, case):
     B, k, V, dt, temps, window = case
     report = {}
