@@ -228,10 +228,31 @@ def test_host_validation_rejects_without_launch(sv):
 
 
 def test_empty_batch_is_a_no_op(sv):
+    """B = 0: every entry point returns SV_OK at once with empty outputs."""
     z = torch.empty(0, 3, 10, device=DEV)
     out = sv.spec_verify_single(z, torch.empty(0, 4, 10, device=DEV),
                                 torch.empty(0, 3, dtype=torch.int32, device=DEV), None)
     assert out["accept_len"].numel() == 0
+    i32 = dict(dtype=torch.int32, device=DEV)
+    tok, temp = torch.empty(0, 3, **i32), torch.empty(0, dtype=torch.float32, device=DEV)
+    table, lens = torch.empty(0, 5, **i32), torch.empty(0, **i32)
+    for dt in (torch.float32, torch.bfloat16):
+        ld = torch.empty(0, 3, 10, dtype=dt, device=DEV)
+        li = torch.empty(0, 4, 10, dtype=dt, device=DEV)
+        lf = torch.empty(0, 4, 10, dtype=dt, device=DEV)
+        out = sv.spec_verify_hier(ld, li, lf, tok, temp, window=4)
+        assert out["out_tokens"].shape == (0, 4)
+        for fn in (sv.spec_verify_hier_rollback, sv.spec_verify_hier_rollback_lazy):
+            out = fn(ld, li, lf, tok, temp, table, lens, block_size=16, max_freed=1, window=4)
+            assert out["num_freed"].numel() == 0 and out["freed_blocks"].shape == (0, 1)
+        pend = sv.make_pending(0, 4, 10, dt, DEV)
+        r = sv.spec_verify_tentative_round(ld, li, tok, temp, pend)
+        f = sv.spec_verify_tentative_flush(torch.empty(0, 5, 10, dtype=dt, device=DEV), temp,
+                                           pend, min_pending=1)
+        assert r["accept_len"].numel() == 0 and f["out_tokens"].shape == (0, 5)
+    freed, nf = sv.kv_blocktable_truncate(table, lens, torch.empty(0, **i32), 16, 1)
+    torch.cuda.synchronize()
+    assert freed.shape == (0, 1) and nf.numel() == 0
 
 
 @pytest.mark.parametrize("dt,temps", [("bf16", (1.0,)), ("f32", (0.0, 0.8))])
