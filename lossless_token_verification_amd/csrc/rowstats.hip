@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
     const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
     const int e0 = chunk * CE;
     double T;
-    const Partial p = chunk_stats<DT, false>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+    const Partial p = chunk_stats<DT, false, true, true>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
     if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
     __syncthreads();   // the next item reuses lds
   }
@@ -104,8 +104,8 @@ __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
 
 hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t st,
                              hipEvent_t ev_start, hipEvent_t ev_stop) {
-  // two resident workgroups per CU (the looping kernel holds more registers)
-  constexpr int64_t kListWorkgroups = 512;
+  // three resident workgroups per CU (133 registers for bf16 rows)
+  constexpr int64_t kListWorkgroups = 768;
   const int64_t clear_wg = (a.n_clear + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<unsigned>(std::max<int64_t>(
       1, std::max(clear_wg, std::min(max_items, kListWorkgroups)))));

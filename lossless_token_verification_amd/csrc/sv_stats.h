@@ -135,7 +135,7 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 
 // (l = -inf) adds 0; without it such an element makes T NaN, which the caller
 // detects and answers with a clamped rescan (identical otherwise: the clamp
 // only moves exponents below -1e30).
-template <int DT, bool ENT, bool CLAMP = true>
+template <int DT, bool ENT, bool CLAMP = true, bool REUNPACK = ENT>
 __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds,
                                double& T_out) {
   constexpr int VPE = DT == 1 ? 8 : 4;
@@ -173,13 +173,14 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
     }
     m = fmaxf(fmaxf(m0, m1), xt);
     const bool empty = !(m > -INFINITY);   // no finite element in this thread's share
-    // The entropy variant unpacks the vectors again for its second pass
-    // instead of keeping the first pass's floats live (93 registers instead
-    // of 159: five wavefronts per SIMD instead of three, and a faster
-    // stream); the plain variant is faster keeping them (156 registers).
+    // REUNPACK: unpack the vectors again for the second pass instead of
+    // keeping the first pass's floats live.  The entropy stream takes it (93
+    // registers instead of 159: five wavefronts per SIMD instead of three,
+    // and a faster stream), and so does the looping row-list kernel; the
+    // plain stream is faster keeping them (156 registers).
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i)
-      if constexpr (ENT) asm volatile("" : "+v"(buf[i]));
+      if constexpr (REUNPACK) asm volatile("" : "+v"(buf[i]));
 
     if (greedy) {
       // lowest index attaining the thread's maximum
