@@ -328,11 +328,11 @@ size_t spec_verify_lmhead_workspace_bytes(const spec_verify_desc* desc, int32_t 
  * "Kernmechanismus"); here q at drafted position j is the softmax of
  * h_draft[b, j] . W^T and p the softmax of h_target[b, j] . W^T.  The rule is
  * then exactly spec_verify_single's.  The logits are formed on the matrix
- * cores (bf16 products, fp32 sums) and never stored: the softmax statistics
- * are reduced from each output tile, the logits at the drafted tokens are
- * formed as dot products (fp32 sums), and after the decisions only the rows
- * each sequence draws from (p at the stop position and, for a correction, q
- * there) are recomputed.
+ * cores (bf16 products, fp32 sums) and the logit matrix is never stored: the
+ * softmax statistics are reduced from each output tile, the logits at the
+ * drafted tokens are formed as dot products (fp32 sums), and after the
+ * decisions only the rows each sequence draws from (p at the stop position
+ * and, for a correction, q there) are recomputed, into the workspace.
  *   desc           dtype must be SV_DTYPE_BF16; vocab = V; row_stride = the
  *                  head's row stride in elements (0 => hidden), a multiple
  *                  of 8

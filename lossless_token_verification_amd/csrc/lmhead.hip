@@ -1,12 +1,12 @@
-// LM-head path: the logits of the draft and final exits are never written to
-// memory.  A bf16 GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16) multiplies
+// LM-head path: the logit matrix of the draft and final exits is never written
+// to memory.  A bf16 GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16) multiplies
 // the exits' hidden states by the shared head W [V, d] and reduces each
 // 192 x 384 output tile in its epilogue to the per-(row, vocabulary tile)
 // softmax partials; a merge launch combines them per row and forms the logit
 // at each row's drafted token (one dot product per row).  After the
-// decisions, the same GEMM recomputes only the two rows each sequence draws
-// from (the target row at the stop position and, for a correction, the draft
-// row there).
+// decisions, the same GEMM recomputes into the workspace only the two rows
+// each sequence draws from (the target row at the stop position and, for a
+// correction, the draft row there).
 //
 // In an early-exit model each exit turns its hidden state into a token
 // distribution (HiSpec summary, section 2 "Kernmechanismus"); with a linear
