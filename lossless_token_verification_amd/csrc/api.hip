@@ -780,6 +780,7 @@ int32_t run_flush(const spec_verify_desc* desc, const void* lf, const float* tem
   sa.flags = flags;
   sa.row_list = row_list;   // the pending rows and L_f rows of the flushed sequences
   sa.row_count = row_count;
+  sa.cached_loads = 1;       // the verification below reads the pending rows again
   err = sv::launch_stats_list(sa, p.rows_total * p.nc, st);
   if (err != hipSuccess) return device_error(err, "row statistics launch");
 

@@ -64,8 +64,11 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(StatsArgs a) {
 }
 
 // Row-list mode: the workgroups loop over (listed row, chunk) items.  The
-// first workgroups clear the verification counters as above.
-template <int DT>
+// first workgroups clear the verification counters as above.  CACHED: the
+// rows are loaded with cache-allocating loads (the tentative flush, whose
+// verification reads its pending rows again: 2-3 us less per round and
+// flush; the lazy call is faster with nontemporal loads).
+template <int DT, bool CACHED>
 __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
   constexpr int ES = DT == 1 ? 2 : 4;
   constexpr int CE = kChunkBytes / ES;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_list_kernel(StatsArgs a) {
     const char* rowp = static_cast<const char*>(a.exit_ptr[e]) + static_cast<int64_t>(local) * a.ld * ES;
     const int e0 = chunk * CE;
     double T;
-    const Partial p = chunk_stats<DT, false, true, true>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
+    const Partial p = chunk_stats<DT, false, true, true, CACHED>(rowp, e0, min(a.V, e0 + CE), greedy, s, lds, T);
     if (tid == 0) a.partials[static_cast<int64_t>(row) * a.nc + chunk] = p;
     __syncthreads();   // the next item reuses lds
   }
@@ -109,10 +112,16 @@ hipError_t launch_stats_list(const StatsArgs& a, int64_t max_items, hipStream_t 
   const int64_t clear_wg = (a.n_clear + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<unsigned>(std::max<int64_t>(
       1, std::max(clear_wg, std::min(max_items, kListWorkgroups)))));
-  if (a.dtype == 1)
-    launch_timed(rowstats_list_kernel<1>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
-  else
-    launch_timed(rowstats_list_kernel<0>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
+  if (a.dtype == 1) {
+    if (a.cached_loads)
+      launch_timed(rowstats_list_kernel<1, true>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
+    else
+      launch_timed(rowstats_list_kernel<1, false>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
+  } else if (a.cached_loads) {
+    launch_timed(rowstats_list_kernel<0, true>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
+  } else {
+    launch_timed(rowstats_list_kernel<0, false>, grid, dim3(kThreads), st, ev_start, ev_stop, a);
+  }
   return hipGetLastError();
 }
 

@@ -69,6 +69,9 @@ struct StatsArgs {
   // row_list, written by an earlier launch.
   const int32_t* row_list;
   const int32_t* row_count;
+  // Row-list launch: cache-allocating instead of nontemporal loads (the
+  // tentative flush, whose verification reads the pending rows again).
+  int32_t cached_loads;
 };
 
 // A kernel launch that, given events, has them take the kernel's own start and

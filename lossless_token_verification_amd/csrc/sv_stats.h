@@ -135,7 +135,7 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&x)[DT == 1 ? 8 : 
 // (l = -inf) adds 0; without it such an element makes T NaN, which the caller
 // detects and answers with a clamped rescan (identical otherwise: the clamp
 // only moves exponents below -1e30).
-template <int DT, bool ENT, bool CLAMP = true, bool REUNPACK = ENT>
+template <int DT, bool ENT, bool CLAMP = true, bool REUNPACK = ENT, bool CACHED = false>
 __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, float s, Red* lds,
                                double& T_out) {
   constexpr int VPE = DT == 1 ? 8 : 4;
@@ -154,7 +154,8 @@ __device__ Partial chunk_stats(const char* rowp, int e0, int e1, bool greedy, fl
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
       const int vi = i * kThreads + tid;
-      buf[i] = vi < nfull ? __builtin_nontemporal_load(vp + vi) : u32x4{pad, pad, pad, pad};
+      buf[i] = vi < nfull ? (CACHED ? vp[vi] : __builtin_nontemporal_load(vp + vi))
+                          : u32x4{pad, pad, pad, pad};
     }
     const int tail0 = e0 + nfull * VPE;
     const bool has_tail = tid < e1 - tail0;
