@@ -362,6 +362,33 @@ def test_full_size_hier_with_rollback(sv):
     P.check_floor(report, 0.9)
 
 
+@pytest.mark.parametrize("trial,seed,offset", [(1, 7, 11), (2, 0x123456789ABCDEF, 2 ** 31 + 5)])
+def test_full_size_hier_rollback_more_inputs(sv, trial, seed, offset):
+    """The benchmarked call (verification and KV rollback in one) on two more
+    full-size input sets, seeds and Philox offsets: every sequence against the
+    oracle, and the rolled-back tables against the oracle's rollback."""
+    w = workloads.make("hier", trial, device=DEV)
+    table, lens = w["block_table"].clone(), w["seq_lens"].clone()
+    out = sv.spec_verify_hier_rollback(w["ld_logits"], w["li_logits"], w["lf_logits"],
+                                       w["draft_tokens"], w["temperature"], table, lens,
+                                       block_size=w["block_size"], max_freed=1,
+                                       window=w["window"], seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    wc = P._host(w)
+    ref = P.oracle_hier(wc, seed, offset, w["window"])
+    report = {}
+    P.compare(out, ref, HIER_KEYS, range(w["B"]), True, report,
+              alt=P.alt_hier(wc, seed, offset, w["window"]))
+    print(f"hier trial {trial}:", report)
+    P.check_floor(report, 0.9)
+    t2, l2, f2, n2 = blocktable.kv_blocktable_truncate(
+        wc["block_table"].numpy(), wc["seq_lens"].numpy(), out["num_drop"].cpu().numpy(),
+        w["block_size"], 1)
+    assert np.array_equal(table.cpu().numpy(), t2) and np.array_equal(lens.cpu().numpy(), l2)
+    assert np.array_equal(out["freed_blocks"].cpu().numpy(), f2)
+    assert np.array_equal(out["num_freed"].cpu().numpy(), n2)
+
+
 ROW_CASES = [
     # (kind, dtype, V, temps)
     ("single", "f32", 1000, (1.0, 0.0, 0.7)),
