@@ -117,12 +117,13 @@ def test_lmhead_host_validation(sv):
     assert out["accept_len"].numel() == 0
 
 
-def test_full_size_lmhead(sv):
+@pytest.mark.parametrize("trial,seed,offset", [(0, 0, 0), (1, 99, 12345)])
+def test_full_size_lmhead(sv, trial, seed, offset):
     """B=128, k=4, d=4096, V=128256 (the fused LM-head workload), in the
     benchmark's launch configuration: every sequence's outputs are
     well-formed and every sequence is compared with the oracle."""
-    w = workloads.make("lmhead", 0, device=DEV)
-    out = _run(sv, w, 0, 0)
+    w = workloads.make("lmhead", trial, device=DEV)
+    out = _run(sv, w, seed, offset)
     torch.cuda.synchronize()
     B, k, V = w["B"], w["k"], w["V"]
     a = out["accept_len"].cpu().numpy()
@@ -131,8 +132,8 @@ def test_full_size_lmhead(sv):
     assert ((a >= 0) & (a <= k)).all() and (ne == a + 1).all()
     assert ((toks >= 0) | (np.arange(k + 1)[None] >= ne[:, None])).all() and toks.max() < V
     wc = P._host(w)
-    ref = P.oracle_lmhead(wc, 0, 0)
+    ref = P.oracle_lmhead(wc, seed, offset)
     report = {}
-    P.compare(out, ref, KEYS, range(B), True, report, alt=P.alt_lmhead(wc, 0, 0))
-    print("lmhead full size:", report)
+    P.compare(out, ref, KEYS, range(B), True, report, alt=P.alt_lmhead(wc, seed, offset))
+    print(f"lmhead full size, trial {trial}:", report)
     P.check_floor(report, 0.75)
