@@ -318,18 +318,20 @@ def test_full_size_tiny_1000_trials(sv):
     P.check_floor(report, 0.99)
 
 
-@pytest.mark.parametrize("name", ["batched", "mixed_temp"])
-def test_full_size_single(sv, name):
+@pytest.mark.parametrize("name,trial,seed,offset", [("batched", 0, 0, 0), ("mixed_temp", 0, 0, 0),
+                                                     ("batched", 1, 31, 777),
+                                                     ("mixed_temp", 1, 2 ** 40 + 3, 9)])
+def test_full_size_single(sv, name, trial, seed, offset):
     """Every sequence of the full-size single-stage workloads against the oracle."""
-    w = workloads.make(name, 0, device=DEV)
-    out = _run_single(sv, w, 0, 0)
+    w = workloads.make(name, trial, device=DEV)
+    out = _run_single(sv, w, seed, offset)
     torch.cuda.synchronize()
     wc = P._host(w)
-    ref = P.oracle_single(wc, 0, 0)
+    ref = P.oracle_single(wc, seed, offset)
     report = {}
     P.compare(out, ref, SINGLE_KEYS, range(w["B"]), w["dtype"] == "bf16", report,
-              alt=P.alt_single(wc, 0, 0))
-    print(name, report)
+              alt=P.alt_single(wc, seed, offset))
+    print(name, trial, report)
     P.check_floor(report, 0.9)
 
 
