@@ -104,19 +104,20 @@ def test_lazy_and_dense_alternate_on_one_workspace(sv):
             assert torch.equal(dense[key], lazy[key]), key
 
 
-def test_full_size_lazy_equals_dense(sv):
+@pytest.mark.parametrize("trial,seed,offset", [(0, 0, 3), (2, 17, 2 ** 20 + 1)])
+def test_full_size_lazy_equals_dense(sv, trial, seed, offset):
     """The headline workload through the lazy call: bit-identical to the dense
     call, and every sequence compared with the oracle directly."""
-    w = workloads.make("hier", 0, device=DEV)
-    dense, lazy = _both(sv, w, 0, 3, w["window"])
+    w = workloads.make("hier", trial, device=DEV)
+    dense, lazy = _both(sv, w, seed, offset, w["window"])
     for key in KEYS + ("table", "lens"):
         assert torch.equal(dense[key], lazy[key]), key
     a1 = lazy["accept_len_inter"].cpu().numpy()
     print("full size lazy: mean a1", a1.mean(), "L_f rows read per sequence", (a1 + 1).mean())
     wc = P._host(w)
-    ref = P.oracle_hier(wc, 0, 3, w["window"])
+    ref = P.oracle_hier(wc, seed, offset, w["window"])
     report = {}
     P.compare(lazy, ref, KEYS[:5], range(w["B"]), True, report,
-              alt=P.alt_hier(wc, 0, 3, w["window"]))
+              alt=P.alt_hier(wc, seed, offset, w["window"]))
     print("full size lazy vs oracle:", report)
     P.check_floor(report, 0.9)

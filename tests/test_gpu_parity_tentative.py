@@ -169,26 +169,27 @@ def test_overflow_is_flagged_and_truncated(sv):
     assert torch.equal(pend["rows"].cpu(), w["ld_logits"][:, :cap])
 
 
-def test_full_size_round_and_flush(sv):
+@pytest.mark.parametrize("trial,seed,offset", [(0, 0, 0), (1, 5, 4242)])
+def test_full_size_round_and_flush(sv, trial, seed, offset):
     """B=256 k=8 V=128256 bf16: a round and a flush (min_pending 1) agree with
     the one-call hierarchy's oracle on every sequence (near ties: the oracle's
     outcome or the one with that decision flipped)."""
-    w = workloads.make("hier", 0, device=DEV)
+    w = workloads.make("hier", trial, device=DEV)
     B, k, V = w["B"], w["k"], w["V"]
     cap = k + 1
     pend = sv.make_pending(B, cap, V, torch.bfloat16, DEV)
     r = sv.spec_verify_tentative_round(w["ld_logits"], w["li_logits"], w["draft_tokens"],
-                                       w["temperature"], pend, seed=0, offset=0)
+                                       w["temperature"], pend, seed=seed, offset=offset)
     f = sv.spec_verify_tentative_flush(_pad_rows(w["lf_logits"], cap + 1), w["temperature"],
-                                       pend, min_pending=1, seed=0, offset=0)
+                                       pend, min_pending=1, seed=seed, offset=offset)
     torch.cuda.synchronize()
     wc = P._host(w)
-    ref = P.oracle_hier(wc, 0, 0, w["window"])
+    ref = P.oracle_hier(wc, seed, offset, w["window"])
     got = dict(accept_len_inter=r["accept_len"], accept_len_final=f["accept_len"],
                out_tokens=f["out_tokens"][:, :k + 1], num_emitted=f["num_emitted"])
     report = {}
     P.compare(got, ref, ("accept_len_inter", "accept_len_final", "out_tokens", "num_emitted"),
-              range(B), True, report, alt=P.alt_hier(wc, 0, 0, w["window"]))
-    print("full size round + flush:", report)
+              range(B), True, report, alt=P.alt_hier(wc, seed, offset, w["window"]))
+    print(f"full size round + flush, trial {trial}:", report)
     P.check_floor(report, 0.9)
     assert (pend["count"].cpu() == 0).all()
